@@ -1,0 +1,321 @@
+"""Pins that tie the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function takes an oracle module (the real one, or a copy with
+a planted mistake) and raises AssertionError when the oracle disagrees with
+the fact it checks.  The facts are closed forms and invariants of softmax
+attention, finite differences of the oracle's own forward, an independent
+pure-Python brute force, and PyTorch's float64 CPU attention with autograd.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from brute_attention import brute_backward, brute_forward
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+# --------------------------------------------------------------------------
+# forward closed forms
+# --------------------------------------------------------------------------
+
+def pin_constant_v(orc):
+    """Every V row equal to c gives O_i = c (softmax weights sum to one)."""
+    rng = np.random.default_rng(11)
+    B, N, H, d = 2, 19, 3, 8
+    q, k = _rand(rng, B, N, H, d), _rand(rng, B, N, H, d)
+    c = _rand(rng, d)
+    v = np.broadcast_to(c, (B, N, H, d)).copy()
+    for causal in (False, True):
+        o, _ = orc.attention_forward(q, k, v, 0.7, causal)
+        _close(o, v, 1e-13, f"constant V causal={causal}")
+
+
+def pin_uniform_scores(orc):
+    """Q = 0 (or scale = 0): equal scores give the mean of the visible V rows.
+
+    Non-causal: O_i = mean_j V_j and LSE_i = ln N.  Causal: O_i = mean of
+    V_0..V_i and LSE_i = ln(i + 1).
+    """
+    rng = np.random.default_rng(12)
+    B, N, H, d = 1, 128, 1, 64
+    k, v = _rand(rng, B, N, H, d), _rand(rng, B, N, H, d)
+    q = _rand(rng, B, N, H, d)
+    for qq, scale in ((np.zeros_like(q), 0.125), (q, 0.0)):
+        o, lse = orc.attention_forward(qq, k, v, scale, False)
+        _close(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), 1e-13, "mean V")
+        _close(lse, np.full((B, H, N), math.log(N)), 1e-13, "LSE = ln N")
+        assert abs(math.log(128) - 4.852030263919617) < 1e-15
+        o, lse = orc.attention_forward(qq, k, v, scale, True)
+        run_mean = np.cumsum(v, axis=1) / np.arange(1, N + 1)[None, :, None, None]
+        _close(o, run_mean, 1e-13, "causal running mean of V")
+        _close(lse[0, 0], np.log(np.arange(1, N + 1)), 1e-13, "causal LSE = ln(i+1)")
+
+
+def pin_causal_first_row(orc):
+    """Causal row 0 sees only key 0: O_0 = V_0, LSE_0 = scale * q_0 . k_0."""
+    rng = np.random.default_rng(13)
+    B, N, H, d = 2, 33, 2, 16
+    q, k, v = (_rand(rng, B, N, H, d) for _ in range(3))
+    scale = 0.3
+    o, lse = orc.attention_forward(q, k, v, scale, True)
+    _close(o[:, 0], v[:, 0], 1e-14, "causal O_0 = V_0")
+    want = scale * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0])
+    _close(lse[:, :, 0], want, 1e-13, "causal LSE_0")
+
+
+def pin_single_key(orc):
+    """N = 1: O = V and LSE = scale * q . k."""
+    rng = np.random.default_rng(14)
+    q, k, v = (_rand(rng, 3, 1, 2, 8) for _ in range(3))
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.5, causal)
+        _close(o, v, 1e-15, "N=1 O=V")
+        _close(lse, 0.5 * np.einsum("bnhd,bnhd->bhn", q, k), 1e-14, "N=1 LSE")
+
+
+def pin_dominant_key(orc):
+    """q_i = alpha * k_j with large alpha and orthogonal other keys -> O_i = V_j."""
+    d, N = 16, 16
+    k = np.eye(N, d)[None, :, None, :] * 1.0       # orthonormal keys
+    rng = np.random.default_rng(15)
+    v = _rand(rng, 1, N, 1, d)
+    perm = rng.permutation(N)
+    q = 60.0 * k[:, perm]                           # query i points at key perm[i]
+    o, lse = orc.attention_forward(q, k, v, 1.0, False)
+    # weight of the other keys is (N-1) e^{-60} ~ 1.3e-25
+    _close(o, v[:, perm], 1e-15, "dominant key")
+    _close(lse, np.full((1, 1, N), 60.0), 1e-13, "dominant key LSE")
+
+
+# --------------------------------------------------------------------------
+# forward invariants
+# --------------------------------------------------------------------------
+
+def pin_rows_sum_to_one(orc):
+    """P = rowsoftmax(S) over visible keys: every row sums to 1, masked = 0."""
+    rng = np.random.default_rng(21)
+    n, m, d = 40, 40, 12
+    q, k = _rand(rng, n, d), _rand(rng, m, d)
+    for causal in (False, True):
+        vis = orc.visible_mask(n, m, causal)
+        p, mx, l = orc.row_softmax(orc.scaled_scores(q, k, 0.9), vis)
+        assert np.all(p[~vis] == 0.0)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) <= 1e-13
+        s = 0.9 * (q @ k.T)
+        assert np.allclose(mx, np.where(vis, s, -np.inf).max(axis=1), rtol=0, atol=1e-14)
+
+
+def pin_mask_shape(orc):
+    """Causal: exactly the keys j <= i are visible (lower triangle incl. diagonal)."""
+    vis = orc.visible_mask(7, 7, True)
+    assert np.array_equal(vis, np.tril(np.ones((7, 7), dtype=bool)))
+    assert orc.visible_mask(5, 5, False).all()
+
+
+def pin_kv_permutation(orc):
+    """Non-causal attention is unchanged when K and V rows move together."""
+    rng = np.random.default_rng(22)
+    B, N, H, d = 2, 31, 2, 8
+    q, k, v = (_rand(rng, B, N, H, d) for _ in range(3))
+    perm = rng.permutation(N)
+    o1, l1 = orc.attention_forward(q, k, v, 0.4, False)
+    o2, l2 = orc.attention_forward(q, k[:, perm], v[:, perm], 0.4, False)
+    _close(o1, o2, 1e-13, "permute K,V: O")
+    _close(l1, l2, 1e-13, "permute K,V: LSE")
+
+
+def pin_key_shift(orc):
+    """k_j -> k_j + u for all j: O unchanged, LSE_i shifts by scale * q_i . u."""
+    rng = np.random.default_rng(23)
+    B, N, H, d = 1, 24, 2, 8
+    q, k, v = (_rand(rng, B, N, H, d) for _ in range(3))
+    u = _rand(rng, d)
+    for causal in (False, True):
+        o1, l1 = orc.attention_forward(q, k, v, 0.6, causal)
+        o2, l2 = orc.attention_forward(q, k + u, v, 0.6, causal)
+        _close(o1, o2, 1e-12, "key shift: O")
+        shift = 0.6 * np.einsum("bnhd,d->bhn", q, u)
+        _close(l2 - l1, shift, 1e-12, "key shift: LSE")
+
+
+def pin_linear_in_v(orc):
+    """O is linear in V: O(aV1 + bV2) = a O(V1) + b O(V2)."""
+    rng = np.random.default_rng(24)
+    B, N, H, d = 1, 20, 2, 8
+    q, k, v1, v2 = (_rand(rng, B, N, H, d) for _ in range(4))
+    for causal in (False, True):
+        o1, _ = orc.attention_forward(q, k, v1, 0.5, causal)
+        o2, _ = orc.attention_forward(q, k, v2, 0.5, causal)
+        o3, _ = orc.attention_forward(q, k, 2.0 * v1 - 3.0 * v2, 0.5, causal)
+        _close(o3, 2.0 * o1 - 3.0 * o2, 1e-12, "linear in V")
+
+
+def pin_lse_bounds(orc):
+    """max_j s_ij <= LSE_i <= max_j s_ij + ln(#visible keys of row i)."""
+    rng = np.random.default_rng(25)
+    B, N, H, d = 1, 50, 1, 8
+    q, k, v = (_rand(rng, B, N, H, d) for _ in range(3))
+    for causal in (False, True):
+        _, lse = orc.attention_forward(q, k, v, 1.3, causal)
+        s = 1.3 * (q[0, :, 0] @ k[0, :, 0].T)
+        vis = np.tril(np.ones((N, N), bool)) if causal else np.ones((N, N), bool)
+        mx = np.where(vis, s, -np.inf).max(axis=1)
+        cnt = vis.sum(axis=1)
+        assert np.all(lse[0, 0] >= mx - 1e-12)
+        assert np.all(lse[0, 0] <= mx + np.log(cnt) + 1e-12)
+
+
+def pin_row_subset(orc):
+    """Computing a subset of query rows gives exactly those rows of the full result."""
+    rng = np.random.default_rng(26)
+    B, N, H, d = 2, 45, 2, 8
+    q, k, v = (_rand(rng, B, N, H, d) for _ in range(3))
+    rows = np.array([0, 7, 44, 13, 30])
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.7, causal)
+        o_s, lse_s = orc.attention_forward(q, k, v, 0.7, causal, rows=rows, row_block=2)
+        _close(o_s, o[:, rows], 1e-14, "row subset O")
+        _close(lse_s, lse[:, :, rows], 1e-14, "row subset LSE")
+
+
+# --------------------------------------------------------------------------
+# independent implementations
+# --------------------------------------------------------------------------
+
+def pin_brute_force_forward(orc):
+    """Pure-Python fsum loops agree with the oracle to 1e-12 (N <= 16, d <= 8)."""
+    rng = np.random.default_rng(31)
+    for (n_q, n_k, d, causal) in ((9, 9, 4, False), (13, 13, 8, True), (6, 11, 5, True),
+                                  (11, 6, 3, True), (16, 16, 8, False)):
+        q, k, v = _rand(rng, 1, n_q, 1, d), _rand(rng, 1, n_k, 1, d), _rand(rng, 1, n_k, 1, d)
+        o, lse = orc.attention_forward(q, k, v, 0.8, causal)
+        bo, blse = brute_forward(q[0, :, 0].tolist(), k[0, :, 0].tolist(),
+                                 v[0, :, 0].tolist(), 0.8, causal)
+        _close(o[0, :, 0], np.array(bo), 1e-12, f"brute O {n_q}x{n_k} causal={causal}")
+        want = np.array(blse)
+        got = lse[0, 0]
+        assert np.array_equal(np.isinf(got), np.isinf(want))
+        fin = np.isfinite(want)
+        _close(got[fin], want[fin], 1e-12, "brute LSE")
+
+
+def pin_brute_force_backward(orc):
+    """Pure-Python chain rule agrees with the oracle's gradients to 1e-12."""
+    rng = np.random.default_rng(32)
+    for (n, d, causal) in ((7, 4, False), (10, 6, True), (16, 8, True)):
+        q, k, v, do = (_rand(rng, 1, n, 1, d) for _ in range(4))
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.7, causal)
+        bq, bk, bv = brute_backward(q[0, :, 0].tolist(), k[0, :, 0].tolist(),
+                                    v[0, :, 0].tolist(), do[0, :, 0].tolist(), 0.7, causal)
+        _close(dq[0, :, 0], np.array(bq), 1e-12, "brute dQ")
+        _close(dk[0, :, 0], np.array(bk), 1e-12, "brute dK")
+        _close(dv[0, :, 0], np.array(bv), 1e-12, "brute dV")
+
+
+def pin_torch_float64(orc):
+    """torch CPU float64 scaled_dot_product_attention + autograd agree to 1e-12."""
+    import torch
+
+    rng = np.random.default_rng(33)
+    B, N, H, d = 2, 37, 3, 16
+    q, k, v, do = (_rand(rng, B, N, H, d) for _ in range(4))
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), dtype=torch.float64,
+                                   requires_grad=True) for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, scale=0.35)
+        to.backward(torch.tensor(do.transpose(0, 2, 1, 3), dtype=torch.float64))
+        o, lse = orc.attention_forward(q, k, v, 0.35, causal)
+        _close(o, to.detach().numpy().transpose(0, 2, 1, 3), 1e-12, "torch O")
+        s = 0.35 * torch.matmul(tq.detach(), tk.detach().transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), -float("inf"))
+        _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, "torch LSE")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.35, causal)
+        for name, mine, ref in (("dQ", dq, tq.grad), ("dK", dk, tk.grad), ("dV", dv, tv.grad)):
+            _close(mine, ref.numpy().transpose(0, 2, 1, 3), 1e-12, f"torch {name}")
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def pin_finite_differences(orc):
+    """Central differences of L = sum(O * dO) match the gradients (rel 1e-6)."""
+    rng = np.random.default_rng(41)
+    eps = 1e-6
+    for (n, d, causal) in ((5, 3, False), (6, 4, True), (8, 4, True)):
+        q, k, v, do = (_rand(rng, 1, n, 1, d) for _ in range(4))
+        scale = 0.9
+        grads = orc.attention_backward(q, k, v, do, scale, causal)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attention_forward(qq, kk, vv, scale, causal)
+            return float(np.sum(o * do))
+
+        for which, g in zip(range(3), grads):
+            fd = np.zeros_like(g)
+            for idx in np.ndindex(*g.shape):
+                args_p = [q.copy(), k.copy(), v.copy()]
+                args_m = [q.copy(), k.copy(), v.copy()]
+                args_p[which][idx] += eps
+                args_m[which][idx] -= eps
+                fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            rel = np.max(np.abs(fd - g)) / max(np.max(np.abs(g)), 1e-300)
+            assert rel <= 1e-6, f"finite differences arg {which} causal={causal}: rel {rel:.2e}"
+
+
+def pin_gradient_identities(orc):
+    """sum_j dV_j = sum_i dO_i;  sum_j dK_j = 0;  causal dQ_0 = 0;
+    constant V gives dQ = dK = 0;  dV is linear in dO."""
+    rng = np.random.default_rng(42)
+    B, N, H, d = 2, 23, 2, 8
+    q, k, v, do, do2 = (_rand(rng, B, N, H, d) for _ in range(5))
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.5, causal)
+        _close(dv.sum(axis=1), do.sum(axis=1), 1e-12, "sum dV = sum dO")
+        _close(dk.sum(axis=1), np.zeros((B, H, d)), 1e-12, "sum dK = 0")
+        if causal:
+            _close(dq[:, 0], np.zeros((B, H, d)), 1e-14, "causal dQ_0 = 0")
+        vc = np.broadcast_to(_rand(rng, d), v.shape).copy()
+        dq_c, dk_c, _ = orc.attention_backward(q, k, vc, do, 0.5, causal)
+        _close(dq_c, np.zeros_like(dq_c), 1e-12, "constant V: dQ = 0")
+        _close(dk_c, np.zeros_like(dk_c), 1e-12, "constant V: dK = 0")
+        _, _, dv2 = orc.attention_backward(q, k, v, do2, 0.5, causal)
+        _, _, dv3 = orc.attention_backward(q, k, v, 3.0 * do - do2, 0.5, causal)
+        _close(dv3, 3.0 * dv - dv2, 1e-12, "dV linear in dO")
+
+
+ALL_PINS = [
+    pin_constant_v,
+    pin_uniform_scores,
+    pin_causal_first_row,
+    pin_single_key,
+    pin_dominant_key,
+    pin_rows_sum_to_one,
+    pin_mask_shape,
+    pin_kv_permutation,
+    pin_key_shift,
+    pin_linear_in_v,
+    pin_lse_bounds,
+    pin_row_subset,
+    pin_brute_force_forward,
+    pin_brute_force_backward,
+    pin_torch_float64,
+    pin_finite_differences,
+    pin_gradient_identities,
+]
