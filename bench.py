@@ -1,0 +1,274 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path: fa_fwd on the long-context forward
+batch (B=1, H=32, N=32768, d=128, causal) and fa_bwd on the backward batch
+(B=4, H=16, N=4096, d=128, causal; its O and LSE come from fa_fwd on the
+same batch, computed before timing).  Inputs are seeded synthetic bf16
+tensors already resident in HBM.  Useful flops: forward 4 B H N^2 d, halved
+when causal; backward 2.5x the forward of its batch (five matrix products
+per tile pair, the recomputation of the scores included).
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
+GPU only (attention heads are independent, see the design notes for how
+it would shard).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+FWD = dict(name="fwd_b1_h32_n32768_d128_causal", B=1, H=32, N=32768, d=128, causal=True)
+BWD = dict(name="bwd_b4_h16_n4096_d128_causal", B=4, H=16, N=4096, d=128, causal=True)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_b1_h32_n32768_d128_causal_hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
+
+
+def fwd_flops(c) -> float:
+    f = 4.0 * c["B"] * c["H"] * c["N"] ** 2 * c["d"]
+    return f / 2 if c["causal"] else f
+
+
+def bwd_flops(c) -> float:
+    return 2.5 * fwd_flops(c)
+
+
+def fwd_algorithmic_bytes(c) -> float:
+    """HBM bytes the forward must move: read Q, K, V, write O (bf16), write LSE (fp32)."""
+    t = c["B"] * c["N"] * c["H"] * c["d"] * 2
+    return 4 * t + c["B"] * c["H"] * c["N"] * 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel changed since."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def device_tensor(bits, device):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def cpu_baseline(fwd_inp, bwd_inp, budget_s: float = 20.0):
+    """Time the fp64 oracle on a bounded sample of the same step: the forward
+    of whole heads of the long-context batch, then the backward of heads of
+    the backward batch, until about ``budget_s`` seconds have been spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    scale = 1.0 / math.sqrt(FWD["d"])
+    useful = 0.0
+    t0 = time.perf_counter()
+    f_heads = 0
+    # forward: one whole head at a time (every query row of that head)
+    while time.perf_counter() - t0 < 0.6 * budget_s and f_heads < FWD["H"]:
+        h = f_heads
+        q = fwd_inp.q[:, :, h:h + 1]
+        k = fwd_inp.k[:, :, h:h + 1]
+        v = fwd_inp.v[:, :, h:h + 1]
+        oracle.attention_forward(q, k, v, scale, True)
+        useful += fwd_flops(dict(FWD, H=1))
+        f_heads += 1
+    t_f = time.perf_counter() - t0
+    b_heads = 0
+    t1 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and b_heads < BWD["B"] * BWD["H"]:
+        b, h = divmod(b_heads, BWD["H"])
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        oracle.attention_backward(bwd_inp.q[sl], bwd_inp.k[sl], bwd_inp.v[sl], bwd_inp.do[sl],
+                                  scale, True)
+        useful += bwd_flops(dict(BWD, B=1, H=1))
+        b_heads += 1
+    t_b = time.perf_counter() - t1
+    total = t_f + t_b
+    return {
+        "value": useful / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: forward of {f_heads} whole head(s) of the "
+                   f"B=1 H=32 N=32768 d=128 causal batch ({t_f:.1f} s) + backward of {b_heads} "
+                   f"head(s) of the B=4 H=16 N=4096 d=128 causal batch ({t_b:.1f} s); "
+                   f"useful-flop convention as the GPU value"),
+        "seconds": round(total, 2),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this attention path runs on ONE GPU only (asked for {args.gpus}); "
+              "heads are independent and would shard across GPUs without communication, "
+              "but no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from io_aware_tiled_fa_amd import binding
+    from io_aware_tiled_fa_amd.inputs import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    binding.load_library()
+
+    print(f"# generating inputs", file=sys.stderr, flush=True)
+    fin = make_workload(FWD["name"])
+    bin_ = make_workload(BWD["name"])
+    fq, fk, fv = (device_tensor(getattr(fin, n + "_bits"), dev) for n in ("q", "k", "v"))
+    bq, bk, bv, bdo = (device_tensor(getattr(bin_, n + "_bits"), dev) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(128)
+    fo = torch.empty_like(fq)
+    flse = torch.empty((FWD["B"], FWD["H"], FWD["N"]), dtype=torch.float32, device=dev)
+    bo, blse = binding.forward(bq, bk, bv, causal=True, scale=scale)
+    bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+    ws = torch.empty(binding.bwd_workspace_size(BWD["B"], BWD["H"], BWD["N"], BWD["d"]),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        binding.forward(fq, fk, fv, causal=True, scale=scale, out=fo, lse=flse)
+        if evs is not None:
+            evs[1].record()
+        binding.backward(bq, bk, bv, bo, blse, bdo, causal=True, scale=scale,
+                         dq=bdq, dk=bdk, dv=bdv, workspace=ws)
+        if evs is not None:
+            evs[2].record()
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+    ff, bf = fwd_flops(FWD), bwd_flops(BWD)
+    f_med, b_med = statistics.median(fwd_ms), statistics.median(bwd_ms)
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    fwd_tf = ff / (f_med * 1e-3) / 1e12
+    bwd_tf = bf / (b_med * 1e-3) / 1e12
+    value = (ff + bf) / (ms_step * 1e-3) / 1e12
+    achieved = ff / (fwd_avg * 1e-3) / 1e12
+
+    def pct(xs, p):
+        xs = sorted(xs)
+        return xs[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
+
+    rec = {
+        "metric": "attention fwd/bwd TFLOP/s at 1 GPU + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1), rounded to bf16)",
+        "config": {
+            "workload": "fa_fwd B=1 H=32 N=32768 d=128 causal + fa_bwd B=4 H=16 N=4096 d=128 causal",
+            "fwd": {"B": 1, "H": 32, "N": 32768, "d": 128, "causal": True, "scale": "1/sqrt(d)"},
+            "bwd": {"B": 4, "H": 16, "N": 4096, "d": 128, "causal": True, "scale": "1/sqrt(d)"},
+            "parallelism": "single GPU",
+        },
+        "fwd": {
+            "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+            "ms_median": round(f_med, 4), "ms_p10": round(pct(fwd_ms, 0.1), 4),
+            "ms_p90": round(pct(fwd_ms, 0.9), 4), "useful_tflop": round(ff / 1e12, 4),
+        },
+        "bwd": {
+            "tflops": round(bwd_tf, 2), "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+            "ms_median": round(b_med, 4), "ms_p10": round(pct(bwd_ms, 0.1), 4),
+            "ms_p90": round(pct(bwd_ms, 0.9), 4), "useful_tflop": round(bf / 1e12, 4),
+        },
+        "roofline": {
+            "kernel": "fwd_kernel<128,4,64,causal>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic(),
+            "algorithmic_bytes": fwd_algorithmic_bytes(FWD),
+            "avg_launch_ms": round(fwd_avg, 4),
+        },
+        "cpu_baseline": None,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(fin, bin_, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

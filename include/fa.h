@@ -1,0 +1,118 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * What the library computes
+ * -------------------------
+ * Exact softmax attention, O = softmax(scale * Q K^T) V, evaluated tile by
+ * tile with a running (online) row maximum and row sum so that the N x N
+ * score matrix never reaches HBM, and the gradients of that attention,
+ * recomputing the probabilities from Q, K and the saved per-row
+ * log-sum-exp instead of storing them.  The pages this follows:
+ *   - "Flash Attention Explained: How IO-Aware Computing Made Long Context
+ *     Practical" (institutepm.com), section "How Flash Attention Fixes It:
+ *     Tiling and Recomputation": tile the input, fuse into one kernel,
+ *     compute softmax incrementally, recompute during the backward pass;
+ *   - "What Is Flash Attention? The Real Speed and Memory Gains, Explained"
+ *     (bestllmfor.com), section "How Flash Attention works" (tiling and
+ *     recomputation; the result is exact up to floating-point rounding);
+ *   - the interface shape (Q, K, V as [batch, seq_len, num_heads, head_dim],
+ *     a softmax scale defaulting to 1/sqrt(head_dim), a causal flag) is the
+ *     one in the holysheep.ai review, "Implementing Flash Attention in Your
+ *     Architecture", and its shape checks in "Common Errors and Fixes",
+ *     Error 4.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are caller-owned DEVICE memory.  bf16 tensors are contiguous
+ *    [B, N, H, d] (BSHD) with element (b, n, h, c) at ((b*N + n)*H + h)*d + c.
+ *    The log-sum-exp is contiguous float32 [B, H, N].
+ *  - Base pointers must be 16-byte aligned.  Outputs must not alias inputs.
+ *  - d must be 64 or 128.  N must be a positive multiple of 64 (tile size of
+ *    the kernels).  B, H >= 1, and B*N*H*d must fit in 2^31 - 1 elements.
+ *  - scale is any finite float (0 allowed; negative allowed).
+ *  - causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *  - stream is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work and return; results are valid once the stream is
+ *    synchronised.  The library allocates no memory and keeps no state
+ *    beyond its loaded kernels.
+ *  - Every argument is validated before any HIP call.  On a bad argument
+ *    nothing is launched and a negative FA_ERR_* code is returned.  A failed
+ *    launch returns FA_ERR_LAUNCH.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = -2,      /* B, H or N not positive, or the size overflows   */
+  FA_ERR_HEADDIM = -3,    /* d is not 64 or 128                              */
+  FA_ERR_SEQLEN = -4,     /* N is not a multiple of the 64-row tile          */
+  FA_ERR_ALIGN = -5,      /* a base pointer is not 16-byte aligned           */
+  FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required         */
+  FA_ERR_SCALE = -7,      /* scale is NaN or infinite                        */
+  FA_ERR_LAUNCH = -8,     /* the HIP launch reported an error                */
+  FA_ERR_ARG = -9         /* causal not 0/1, or outputs alias inputs         */
+} fa_status;
+
+/*
+ * Forward pass.
+ *   q, k, v : bf16 [B, N, H, d] inputs.
+ *   o       : bf16 [B, N, H, d] output, O = softmax(scale * Q K^T) V, rows
+ *             normalised, rounded to bf16 (round to nearest even).
+ *   lse     : float32 [B, H, N] output, lse[b,h,i] = ln sum_j exp(s_ij) over
+ *             the visible keys of row i, where s_ij = scale * q_i . k_j (the
+ *             natural-log log-sum-exp of the scaled scores).  The backward
+ *             pass consumes it.
+ * Accumulation is float32; QK^T and PV run on bf16 matrix cores with the
+ * probabilities rounded to bf16 before the PV product.
+ * Returns FA_OK or an FA_ERR_* code (see the conventions above).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape: a float32 [B, H, N]
+ * row term D_i = sum_c dO_ic * O_ic and a float32 [B, N, H, d] dQ
+ * accumulator, each 256-byte aligned.  Returns 0 for an invalid shape.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass by recomputation.
+ *   q, k, v, o : bf16 [B, N, H, d], the forward's inputs and its output O.
+ *   lse        : float32 [B, H, N] from fa_fwd with the same arguments.
+ *   dO         : bf16 [B, N, H, d], gradient of the loss with respect to O.
+ *   dq, dk, dv : bf16 [B, N, H, d] outputs, gradients of the loss with
+ *                respect to q, k and v (float32 accumulation, rounded to
+ *                bf16 at the end).
+ *   workspace  : device memory of at least fa_bwd_workspace_size(B,H,N,d)
+ *                bytes, 256-byte aligned, caller-owned; its contents on
+ *                entry do not matter and are overwritten.
+ * The probabilities are recomputed tile by tile as exp(s_ij - lse_i); the
+ * score and probability matrices are never stored.  dQ is accumulated with
+ * float32 atomic adds, so its last bits may differ from run to run.
+ * Returns FA_OK or an FA_ERR_* code.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,145 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation, the
+// backward workspace layout, and dispatch to the gfx950 kernels.
+//
+// Shape checks mirror the ones the holysheep.ai review prints for its
+// interface ("Common Errors and Fixes", Error 4: four-dimensional
+// [batch, seq_len, num_heads, head_dim] tensors with matching batch, heads
+// and head_dim, and equal K / V lengths); here every tensor has one shape,
+// so they reduce to positive B, H, N and a supported d.  The same page
+// ("Common Errors and Fixes", Error 1) notes that a launch fails when a
+// tile exceeds device limits; here unsupported sizes are refused before
+// anything is launched.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kTile = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+fa_status check_shape(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const long long elems = (long long)B * N * H * d;
+  if (elems > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
+  if (N % kTile != 0) return FA_ERR_SEQLEN;
+  return FA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H and N must be positive and B*N*H*d must fit in 2^31-1";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_SEQLEN: return "sequence length N must be a multiple of 64";
+    case FA_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than fa_bwd_workspace_size()";
+    case FA_ERR_SCALE: return "scale must be a finite float";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ARG: return "causal must be 0 or 1 and outputs must not overlap inputs";
+  }
+  return "unknown status";
+}
+
+int fa_version(void) { return 100; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  const size_t tb = (size_t)B * N * H * d * 2, lb = (size_t)B * H * N * 4;
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins)
+    if (overlaps(o, tb, in, tb) || overlaps(lse, lb, in, tb)) return FA_ERR_ARG;
+  if (overlaps(o, tb, lse, lb)) return FA_ERR_ARG;
+
+  fa::FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.c = fabsf(scale) * 1.4426950408889634f;
+  a.negate = scale < 0.f;
+  const hipError_t e = fa::launch_fwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round256(2 * rows * sizeof(float)) + round256((size_t)B * N * H * d * sizeof(float));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  const void* all[] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : all)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FA_ERR_WORKSPACE;
+  const size_t tb = (size_t)B * N * H * d * 2, lb = (size_t)B * H * N * 4;
+  const void* ins[6] = {q, k, v, o, dO, lse};
+  const size_t insz[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outsz[4] = {tb, tb, tb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.lse = lse;
+  a.dO = static_cast<const __bf16*>(dO);
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.drow = static_cast<float*>(workspace);
+  a.dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(2 * (size_t)B * H * N * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_bwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

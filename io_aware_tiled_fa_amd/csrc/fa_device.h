@@ -1,0 +1,98 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// vector types, the bf16 matrix-core instructions, lane-layout facts of
+// those instructions, cross-half lane exchange and LDS helpers.
+//
+// Lane layouts used throughout (checked on gfx950 hardware):
+//  * v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] * B[16x32], wave64:
+//      A: lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//      B: lane l holds B[8 * (l / 32) + e][l % 32], e = 0..7
+//      C: lane l holds C[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32], e = 0..15
+//    The contraction index only has to agree between A and B, so any
+//    consistent relabelling of (l / 32, e) -> k gives the same product.
+//  * ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+//    (i % 4) of the 8-byte chunks read by lanes i/4, i/4 + 4, i/4 + 8 and
+//    i/4 + 12 of its group (a 4 x 16 transpose of 16-bit values).
+//  * v_permlane32_swap(a, b): swaps the upper 32 lanes of a with the lower
+//    32 lanes of b; with a == b the pair holds (x[l], x[l ^ 32]) per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// max(x[l], x[l ^ 32]) in every lane
+__device__ __forceinline__ float max_cross_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// x[l] + x[l ^ 32] in every lane
+__device__ __forceinline__ float sum_cross_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// 16-byte asynchronous copy global -> LDS.  Lane l writes bytes
+// [lds + 16 l, lds + 16 l + 16); lds must be the same in every lane.
+__device__ __forceinline__ void copy16_to_lds(const void* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// wait until every outstanding vector-memory load of this wave has landed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const lds_char* p) { return *(const lds_bf16x8*)p; }
+
+// XOR swizzle of the 16-byte chunk index of an LDS tile row.  For 128-wide
+// rows it makes both the 32-row b128 reads of a K tile and the 4-row
+// transpose reads of a V tile hit distinct banks; likewise for 64-wide rows.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return ((row >> 2) & 1) | (((row >> 3) & 1) << 1) | (((row >> 1) & 1) << 2);
+  }
+}
+
+}  // namespace fa

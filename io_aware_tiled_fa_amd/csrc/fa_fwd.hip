@@ -1,0 +1,285 @@
+// Forward attention kernel for gfx950: O = softmax(scale * Q K^T) V and the
+// per-row log-sum-exp, one pass over K and V per query tile.
+//
+// The method is the one the pages describe ("Flash Attention Explained:
+// How IO-Aware Computing Made Long Context Practical", institutepm.com,
+// section "How Flash Attention Fixes It: Tiling and Recomputation"): load
+// small tiles of Q, K and V into on-chip memory, fuse the score product,
+// the softmax and the product with V into one kernel so no intermediate
+// reaches HBM, and keep a running row maximum and row sum so the softmax is
+// built up tile by tile and still ends exact.  The pages give no tile sizes
+// or listing; everything below the statement of the method is designed for
+// CDNA4:
+//
+//  * one workgroup = NW wave64s, each wave owning 32 query rows (Br = 32 NW);
+//    the query tile lives in VGPRs for the whole kernel;
+//  * K and V tiles of BC keys stream through LDS, double buffered, copied
+//    straight from HBM into LDS (global_load_lds, no VGPR staging) with an
+//    XOR chunk swizzle so the matrix-core operand reads are conflict free;
+//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    so every lane holds 32 scores of ONE query row: the row max needs one
+//    cross-half exchange, the row sum none until the end, and the rescale
+//    factor is lane-local;
+//  * the bf16 probabilities stay in registers and feed O^T += V^T P^T as the
+//    B operand directly; V^T comes from LDS through transpose reads;
+//  * softmax works in base 2 with scale*log2(e) folded into one FMA; the
+//    running maximum is only moved (and O rescaled) when it grows by more
+//    than 2^8, which keeps the result exact (O and the sum share the stale
+//    maximum) and skips most rescale passes;
+//  * causal: key tiles after a query tile's last row are never loaded; only
+//    tiles straddling the diagonal are masked (key j visible iff j <= i);
+//  * workgroup order: heaviest causal query tiles first, and each XCD
+//    (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
+//    set of heads so the query tiles sharing K and V share an L2.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+  constexpr int BR = NW * 32;
+  constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
+  constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
+  constexpr int NCH = D / 8;             // 16-byte chunks per row
+  constexpr int LOADS = TILEB / 1024;    // 1 KiB wave copies per tile
+  constexpr int LPW = LOADS / NW;        // copies per wave per tile
+  constexpr int NSB = BC / 32;           // 32-key sub-blocks of a tile
+  constexpr int NDB = D / 32;            // 32-wide column blocks of O
+  constexpr int NKK = D / 16;            // k-steps of the score product
+  constexpr int NT = BC / 16;            // k-steps of the PV product
+  static_assert(LOADS % NW == 0, "tile copies must split evenly over waves");
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILEB];  // K0 K1 V0 V1
+  lds_char* smem = (lds_char*)smem_raw;
+
+  // ---- workgroup -> (batch, head, query tile)
+  const int nqb = (a.N + BR - 1) / BR;
+  const int nbh = a.B * a.H;
+  const int wg = blockIdx.x;
+  int bh, qi;
+  if ((nbh & 7) == 0) {
+    const int hpx = nbh >> 3;  // heads per XCD
+    const int x = wg & 7, s = wg >> 3;
+    bh = x * hpx + s % hpx;
+    qi = s / hpx;
+  } else {
+    bh = wg % nbh;
+    qi = wg / nbh;
+  }
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int b = bh / a.H, h = bh - b * a.H;
+
+  const int w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int h2 = l >> 5;   // which half of the wave
+  const int l32 = l & 31;  // query row of this lane within the wave's 32
+  const int q0 = qb * BR;
+  const int qw = q0 + 32 * w;
+  const bool wave_active = qw < a.N;
+
+  const size_t rs = (size_t)a.H * D;  // elements between consecutive rows
+  const size_t head_off = (size_t)b * a.N * rs + (size_t)h * D;
+  const __bf16* kbase = a.k + head_off;
+  const __bf16* vbase = a.v + head_off;
+
+  // ---- Q tile -> B operand registers (lane: row l32, d = 16 kk + 8 h2 .. +7)
+  bf16x8 qop[NKK];
+  if (wave_active) {
+    const __bf16* qrow = a.q + head_off + (size_t)(qw + l32) * rs + 8 * h2;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qop[kk] = *(const bf16x8*)(qrow + 16 * kk);
+    if (a.negate) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 t = __builtin_bit_cast(u32x4, qop[kk]) ^ 0x80008000u;
+        qop[kk] = __builtin_bit_cast(bf16x8, t);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qop[kk] = bf16x8{};
+  }
+
+  // ---- per-lane LDS read offsets
+  // K operand of S^T = K Q^T: row 32 s + l32, chunk 2 kk + h2.
+  int koff[NKK];
+  {
+    const int sw = chunk_swizzle<D>(l32);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + h2) ^ sw) << 4);
+  }
+  // V^T operand by transpose reads: group g = l / 16, lane j = l % 16 reads
+  // row 16 t + 4 h2 + j / 4 (+ 8 for the second read), columns
+  // 32 dblk + 16 (g % 2) + 4 (j % 4) .. +3.
+  int voff[2][NDB];
+  {
+    const int g = l >> 4, j = l & 15;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 4 * h2 + (j >> 2) + 8 * r;
+      const int sw = chunk_swizzle<D>(row);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int ch = 4 * db + 2 * (g & 1) + ((j & 3) >> 1);
+        voff[r][db] = row * ROWB + ((ch ^ sw) << 4) + 8 * (j & 1);
+      }
+    }
+  }
+  // direct HBM -> LDS copies: wave copy c = w + NW i fills LDS bytes
+  // [1024 c, 1024 c + 1024) of a tile; lane l fills 16-byte slot 64 c + l,
+  // i.e. tile row p / NCH, swizzled chunk p % NCH.
+  int goff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = 64 * (w + NW * i) + l;
+    const int row = p / NCH, ch = p % NCH;
+    goff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const __bf16* kg = kbase + (size_t)kt * BC * rs;
+    const __bf16* vg = vbase + (size_t)kt * BC * rs;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int c = w + NW * i;
+      copy16_to_lds(kg + goff[i], (lds_void*)(smem + buf * TILEB + c * 1024));
+      copy16_to_lds(vg + goff[i], (lds_void*)(smem + (2 + buf) * TILEB + c * 1024));
+    }
+  };
+
+  // ---- key tiles this workgroup visits
+  const int ntiles_all = a.N / BC;
+  int ntiles = ntiles_all;
+  if (CAUSAL) {
+    const int last_row = min(q0 + BR, a.N) - 1;
+    ntiles = min(ntiles_all, last_row / BC + 1);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_run = -__builtin_inff();  // running max, base-2 scaled units
+  float l_run = 0.f;                // this lane's half of the running sum
+  const float c = a.c;
+  const int qrow = qw + l32;
+
+  issue_tile(0, 0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue_tile(kt + 1, (kt + 1) & 1);
+    const int kb = kt * BC;
+    if (!wave_active) continue;
+    if (CAUSAL && kb > qw + 31) continue;  // whole tile in this wave's future
+    const lds_char* kt_lds = smem + (kt & 1) * TILEB;
+    const lds_char* vt_lds = smem + (2 + (kt & 1)) * TILEB;
+
+    // S^T (keys x queries) for each 32-key sub-block
+    f32x16 sacc[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      sacc[sb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sacc[sb] = mfma32(lds_read16(kt_lds + sb * 32 * ROWB + koff[kk]), qop[kk], sacc[sb]);
+    }
+
+    // causal mask on tiles crossing the diagonal: key > query -> -inf
+    const bool diag = CAUSAL && (kb + BC - 1 > qw);
+    if (diag) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          if (key > qrow) sacc[sb][e] = -__builtin_inff();
+        }
+    }
+
+    // row max of this tile (raw scores), then in scaled base-2 units
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
+    mx = max_cross_half(mx);
+    const float mblk = (mx == -__builtin_inff()) ? mx : mx * c;
+    const float mnew = fmaxf(m_run, mblk);
+    const bool need = mnew > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_run - mnew) : 1.0f;
+      if (need) m_run = mnew;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      l_run *= alpha;
+    }
+
+    // probabilities, rounded to bf16 pairs for the PV product
+    const float negm = -m_run;
+    uint32_t pk[NSB][8];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
+        float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
+        if (diag) {
+          const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          p0 = (key > qrow) ? 0.f : p0;
+          p1 = (key + 1 > qrow) ? 0.f : p1;
+        }
+        l_run += p0 + p1;
+        pk[sb][e >> 1] = pack_bf16x2(p0, p1);
+      }
+
+    // O^T += V^T P^T over the tile's keys, 16 at a time
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int sb = t >> 1, hf = t & 1;
+      u32x4 pv = {pk[sb][4 * hf + 0], pk[sb][4 * hf + 1], pk[sb][4 * hf + 2], pk[sb][4 * hf + 3]};
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x4 v0 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[0][db]);
+        const bf16x4 v1 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[1][db]);
+        const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = mfma32(vop, pop, oacc[db]);
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  // ---- epilogue: O = O_acc / l in bf16, LSE = (m + log2 l) ln 2
+  const float lt = sum_cross_half(l_run);
+  const float inv = fast_rcp(lt);
+  __bf16* orow = a.o + head_off + (size_t)qrow * rs;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * db + 8 * g4 + 4 * h2;
+      u32x2 val = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                   pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+      *(u32x2*)(orow + d0) = val;
+    }
+  if (h2 == 0) a.lse[((size_t)b * a.H + h) * a.N + qrow] = (m_run + fast_log2(lt)) * kLn2;
+}
+
+template <int D, int NW, int BC, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BR = NW * 32;
+  const int nqb = (a.N + BR - 1) / BR;
+  dim3 grid((unsigned)(a.B * a.H * nqb));
+  dim3 block(NW * 64);
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, CAUSAL>, grid, block, args, 0, stream);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_fwd_t<128, 4, 64, true>(a, stream) : launch_fwd_t<128, 4, 64, false>(a, stream);
+  return causal ? launch_fwd_t<64, 4, 64, true>(a, stream) : launch_fwd_t<64, 4, 64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,41 @@
+// Host-visible argument blocks and launchers of the attention kernels
+// (internal to libfa.so; the public interface is include/fa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int B, H, N;
+  float c;     // |scale| * log2(e): scores are used in base-2 units
+  int negate;  // scale < 0: the query is negated in registers instead
+};
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const float* lse;
+  const __bf16* dO;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* drow;   // [B, H, N] row term sum_c dO * O
+  float* dqacc;  // [B, N, H, d] float32 dQ accumulator
+  int B, H, N;
+  float scale;   // signed softmax scale
+  float c;       // scale * log2(e) (signed)
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects bad arguments before touching the GPU.
+
+Every call below carries at least one invalid argument, so validation
+returns before any HIP call; the pointer values are never dereferenced.
+"""
+
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_tiled_fa_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(0, -10, -1):
+        s = lib.fa_status_string(code)
+        assert s and s != b"unknown status", code
+    assert lib.fa_status_string(-99) == b"unknown status"
+    assert lib.fa_version() >= 100
+
+
+# fake, 256-byte aligned device addresses, far apart so nothing overlaps
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=1, N=128, d=64,
+        scale=0.125, causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == -1
+    assert fwd(lib, lse=None) == -1
+    assert fwd(lib, d=96, scale=float("nan")) == -3
+    assert fwd(lib, B=0, scale=float("nan")) == -2
+    assert fwd(lib, H=-1, scale=float("nan")) == -2
+    assert fwd(lib, B=2 ** 20, H=64, N=2 ** 16, d=128) == -2   # > 2^31 elements
+    assert fwd(lib, N=100, scale=float("nan")) == -4
+    assert fwd(lib, N=96, scale=float("nan")) == -4
+    assert fwd(lib, q=P[0] + 8, scale=float("nan")) == -5
+    assert fwd(lib, lse=P[4] + 4, scale=float("nan")) == -5
+    assert fwd(lib, scale=float("nan")) == -7
+    assert fwd(lib, scale=float("inf")) == -7
+    assert fwd(lib, scale=-math.inf) == -7
+    assert fwd(lib, causal=2) == -9
+    assert fwd(lib, o=P[0]) == -9                    # output aliases Q
+    assert fwd(lib, lse=P[2] + 256) == -9            # LSE inside V
+
+
+def bwd(lib, B=1, H=1, N=128, d=64, ws=P[9], ws_bytes=None, scale=0.125, causal=1, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8])
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, N, d)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                      B, H, N, d, scale, causal, ws, ws_bytes, None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, do=None) == -1
+    assert bwd(lib, dv=None) == -1
+    assert bwd(lib, d=32) == -3
+    assert bwd(lib, N=0) == -2
+    assert bwd(lib, N=65) == -4
+    assert bwd(lib, dk=P[7] + 2) == -5
+    assert bwd(lib, ws=None) == -6
+    assert bwd(lib, ws_bytes=1024) == -6
+    assert bwd(lib, ws=P[9] + 16) == -6               # workspace must be 256-byte aligned
+    assert bwd(lib, scale=float("nan")) == -7
+    assert bwd(lib, causal=-1) == -9
+    assert bwd(lib, dq=P[1]) == -9                    # dQ aliases K
+    assert bwd(lib, dk=P[6]) == -9                    # dK aliases dQ
+    assert bwd(lib, ws=P[8]) == -9                    # workspace aliases dV
+
+
+def test_workspace_size(lib):
+    assert lib.fa_bwd_workspace_size(0, 1, 64, 64) == 0
+    assert lib.fa_bwd_workspace_size(1, 1, 64, 80) == 0
+    B, H, N, d = 4, 16, 4096, 128
+    rows = B * H * N * 4 * 2
+    acc = B * N * H * d * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_size(B, H, N, d) == r256(rows) + r256(acc)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    from io_aware_tiled_fa_amd import binding
+
+    q = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.validate_attention_inputs(q, q, q)
+    with pytest.raises(TypeError):
+        binding.validate_attention_inputs(q.float(), q, q)
+    with pytest.raises(ValueError, match="4 dimensions"):
+        binding.validate_attention_inputs(q[0], q, q)

@@ -1,0 +1,82 @@
+"""Backward parity: fa_bwd through the C ABI against the fp64 oracle's
+direct differentiation.  The GPU backward consumes the GPU forward's O and
+LSE; the oracle recomputes everything from Q, K, V and dO in fp64."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_tiled_fa_amd.inputs import make_inputs, make_workload
+from parity import TOL_GRAD, announce, backward_error_bound, compare, to_device, to_numpy_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from io_aware_tiled_fa_amd import binding
+
+    binding.load_library()
+    return binding
+
+
+def run_bwd(fa, inp, causal, scale):
+    import torch
+
+    q, k, v, do = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_bwd(fa, inp, causal, scale, derived_bound=False):
+    dq, dk, dv = run_bwd(fa, inp, causal, scale)
+    rq, rk, rv = oracle.attention_backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    bounds = (None, None, None)
+    if derived_bound:
+        o_ref, _ = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal)
+        bounds = backward_error_bound(inp.q, inp.k, inp.v, inp.do, o_ref, scale, causal)
+    compare("dQ", to_numpy_f32(dq), rq, TOL_GRAD, bound=bounds[0])
+    compare("dK", to_numpy_f32(dk), rk, TOL_GRAD, bound=bounds[1])
+    compare("dV", to_numpy_f32(dv), rv, TOL_GRAD, bound=bounds[2])
+
+
+SMALL = [
+    # B, H, N, d, causal  (N = 192 / 320: the last 128-key block is half full)
+    (1, 1, 64, 128, True),
+    (1, 2, 192, 128, True),
+    (1, 2, 192, 128, False),
+    (2, 3, 256, 64, True),
+    (2, 3, 256, 64, False),
+    (2, 4, 320, 128, True),
+    (1, 8, 512, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL)
+def test_backward_small(fa, B, H, N, d, causal):
+    announce(f"bwd small B={B} H={H} N={N} d={d} causal={causal}")
+    inp = make_inputs(B, H, N, d, seed=2000 + N + d, with_do=True)
+    check_bwd(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.3, 0.0])
+def test_backward_scales(fa, scale):
+    """Outside the five workloads: held to the error bound derived from the
+    bf16 arithmetic (see parity.py) instead of the fixed gate."""
+    announce(f"bwd scale={scale}")
+    inp = make_inputs(1, 2, 256, 128, seed=11, with_do=True)
+    check_bwd(fa, inp, True, scale, derived_bound=True)
+
+
+def test_workload_bwd_b4_h16_n4096_d128_causal(fa):
+    announce("bwd workload B=4 H=16 N=4096 d=128 causal (every element)")
+    inp = make_workload("bwd_b4_h16_n4096_d128_causal")
+    check_bwd(fa, inp, True, 1.0 / math.sqrt(128))

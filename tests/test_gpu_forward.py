@@ -1,0 +1,131 @@
+"""Forward parity: the HIP kernels through the C ABI against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_tiled_fa_amd.inputs import make_inputs, make_workload
+from parity import (TOL_LSE, TOL_O, TOL_O_MEAN, announce, compare, forward_error_bound, sample_rows,
+                    to_device, to_numpy_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from io_aware_tiled_fa_amd import binding
+
+    binding.load_library()
+    return binding
+
+
+def run_fwd(fa, inp, causal, scale):
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    import torch
+
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_fwd(fa, inp, causal, scale, rows=None, derived_bound=False):
+    o, lse = run_fwd(fa, inp, causal, scale)
+    o_np, lse_np = to_numpy_f32(o), lse.cpu().numpy()
+    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal, rows=rows)
+    if rows is not None:
+        o_np, lse_np = o_np[:, rows], lse_np[:, :, rows]
+    bound = forward_error_bound(inp.q, inp.k, inp.v, scale, causal) if derived_bound else None
+    compare("O", o_np, o_ref, TOL_O, None if derived_bound else TOL_O_MEAN, bound=bound)
+    compare("LSE", lse_np, lse_ref, TOL_LSE, ulp_aware=False)
+    return o, lse
+
+
+SMALL = [
+    # B, H, N, d, causal   (N = 320 / 448: query tiles of 128 rows end ragged)
+    (1, 1, 64, 64, False),
+    (1, 1, 64, 128, True),
+    (2, 3, 320, 64, False),
+    (2, 3, 320, 64, True),
+    (2, 3, 320, 128, False),
+    (2, 3, 320, 128, True),
+    (1, 8, 192, 128, True),
+    (2, 8, 256, 64, False),
+    (3, 5, 448, 128, True),
+    (1, 2, 1024, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL)
+def test_forward_small(fa, B, H, N, d, causal):
+    announce(f"fwd small B={B} H={H} N={N} d={d} causal={causal}")
+    inp = make_inputs(B, H, N, d, seed=1000 + N + d)
+    check_fwd(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.0, 0.01])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_scales(fa, scale, causal):
+    """Negative, zero, large and tiny softmax scales (any finite float is legal).
+    Outside the five workloads, so O is held to the error bound derived from
+    the bf16 arithmetic (see parity.py) instead of the fixed gate."""
+    announce(f"fwd scale={scale} causal={causal}")
+    inp = make_inputs(1, 2, 256, 128, seed=7)
+    check_fwd(fa, inp, causal, scale, derived_bound=True)
+
+
+def test_forward_deterministic(fa):
+    import torch
+
+    announce("fwd determinism")
+    inp = make_inputs(2, 4, 512, 128, seed=3)
+    o1, l1 = run_fwd(fa, inp, True, 0.1)
+    o2, l2 = run_fwd(fa, inp, True, 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_causal_single_tile_vs_noncausal_last_row(fa):
+    """With one 64-row tile, the causal last row sees every key: it must
+    equal the non-causal last row bit for bit."""
+    import torch
+
+    inp = make_inputs(1, 1, 64, 64, seed=9)
+    oc, lc = run_fwd(fa, inp, True, 0.125)
+    on, ln = run_fwd(fa, inp, False, 0.125)
+    assert torch.equal(oc[:, -1], on[:, -1])
+    assert torch.equal(lc[..., -1], ln[..., -1])
+
+
+def test_workload_fwd_b1_h1_n128_d64(fa):
+    announce("fwd workload B=1 H=1 N=128 d=64 non-causal (every element)")
+    inp = make_workload("fwd_b1_h1_n128_d64")
+    o, lse = check_fwd(fa, inp, False, 1.0 / 8.0)
+    assert tuple(o.shape) == (1, 128, 1, 64) and tuple(lse.shape) == (1, 1, 128)
+
+
+def test_workload_fwd_b4_h16_n2048_d64(fa):
+    announce("fwd workload B=4 H=16 N=2048 d=64 non-causal (every element)")
+    inp = make_workload("fwd_b4_h16_n2048_d64")
+    check_fwd(fa, inp, False, 1.0 / 8.0)
+
+
+def test_workload_fwd_b2_h32_n8192_d128_causal_peaked(fa):
+    """Sampled rows (each row is exact on its own), every peaked row included."""
+    announce("fwd workload B=2 H=32 N=8192 d=128 causal peaked (sampled rows)")
+    inp = make_workload("fwd_b2_h32_n8192_d128_causal_peaked")
+    rng = np.random.default_rng(0)
+    rows = sample_rows(8192, 96, rng, extra=inp.peaked_rows[0, 0].tolist() + inp.peaked_rows[1, 5].tolist())
+    check_fwd(fa, inp, True, 1.0 / math.sqrt(128), rows=rows)
+
+
+def test_workload_fwd_b1_h32_n32768_d128_causal(fa):
+    announce("fwd workload B=1 H=32 N=32768 d=128 causal (sampled rows)")
+    inp = make_workload("fwd_b1_h32_n32768_d128_causal")
+    rng = np.random.default_rng(1)
+    rows = sample_rows(32768, 48, rng)
+    check_fwd(fa, inp, True, 1.0 / math.sqrt(128), rows=rows)
