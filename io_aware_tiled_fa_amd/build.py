@@ -35,6 +35,9 @@ def flags() -> list:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed fp32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in VGPRs: no AGPR <-> VGPR copies around
+        # the softmax and the rescale of O
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
     ]
 
@@ -45,7 +48,7 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
     cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
-        cmd += ["-save-temps=obj", "-Rpass-analysis=kernel-resource-usage"]
+        cmd += ["-save-temps", "-Rpass-analysis=kernel-resource-usage"]
     cwd = asm_dir if asm_dir else None
     if asm_dir:
         cmd[cmd.index("-o") + 1] = os.path.abspath(tmp)

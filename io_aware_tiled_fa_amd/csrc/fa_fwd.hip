@@ -37,7 +37,7 @@
 namespace fa {
 
 template <int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
   constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
@@ -50,8 +50,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   constexpr int NT = BC / 16;            // k-steps of the PV product
   static_assert(LOADS % NW == 0, "tile copies must split evenly over waves");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILEB];  // K0 K1 V0 V1
-  lds_char* smem = (lds_char*)smem_raw;
+  // Four separate LDS objects (K and V, two buffers each) and a loop unrolled
+  // by two: every access names its buffer at compile time, so the compiler
+  // can see that the copies into one buffer never alias reads of the other
+  // and does not stall the reads on the outstanding copies.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
   // ---- workgroup -> (batch, head, query tile)
   const int nqb = (a.N + BR - 1) / BR;
@@ -136,14 +142,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const int row = p / NCH, ch = p % NCH;
     goff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
   }
-  auto issue_tile = [&](int kt, int buf) {
+  auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) {
     const __bf16* kg = kbase + (size_t)kt * BC * rs;
     const __bf16* vg = vbase + (size_t)kt * BC * rs;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds(kg + goff[i], (lds_void*)(smem + buf * TILEB + c * 1024));
-      copy16_to_lds(vg + goff[i], (lds_void*)(smem + (2 + buf) * TILEB + c * 1024));
+      copy16_to_lds(kg + goff[i], (lds_void*)(kdst + c * 1024));
+      copy16_to_lds(vg + goff[i], (lds_void*)(vdst + c * 1024));
     }
   };
 
@@ -163,25 +169,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const float c = a.c;
   const int qrow = qw + l32;
 
-  issue_tile(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // one key tile: wait for its copies, start the next tile's copies into
+  // the other buffer, then compute on this one
+  auto tile_step = [&](int kt, const lds_char* kt_lds, const lds_char* vt_lds,
+                       lds_char* knext, lds_char* vnext) {
     wait_vmem();
     __syncthreads();
-    if (kt + 1 < ntiles) issue_tile(kt + 1, (kt + 1) & 1);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
     const int kb = kt * BC;
-    if (!wave_active) continue;
-    if (CAUSAL && kb > qw + 31) continue;  // whole tile in this wave's future
-    const lds_char* kt_lds = smem + (kt & 1) * TILEB;
-    const lds_char* vt_lds = smem + (2 + (kt & 1)) * TILEB;
+    if (!wave_active) return;
+    if (CAUSAL && kb > qw + 31) return;  // whole tile in this wave's future
 
-    // S^T (keys x queries) for each 32-key sub-block
+    // S^T (keys x queries) for each 32-key sub-block.  All K operands of a
+    // sub-block are requested from LDS before its first product so the
+    // reads overlap the matrix-core work instead of each product waiting.
     f32x16 sacc[NSB];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
+      bf16x8 kop[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kop[kk] = lds_read16(kt_lds + sb * 32 * ROWB + koff[kk]);
       sacc[sb] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        sacc[sb] = mfma32(lds_read16(kt_lds + sb * 32 * ROWB + koff[kk]), qop[kk], sacc[sb]);
+      for (int kk = 0; kk < NKK; ++kk) sacc[sb] = mfma32(kop[kk], qop[kk], sacc[sb]);
     }
 
     // causal mask on tiles crossing the diagonal: key > query -> -inf
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          if (key > qrow) sacc[sb][e] = -__builtin_inff();
+          sacc[sb][e] = (key > qrow) ? -__builtin_inff() : sacc[sb][e];
         }
     }
 
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
       for (int e = 0; e < 16; e += 2) {
         float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
         float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
-        if (diag) {
+        if (diag) {  // exp2(-inf) is 0 already unless scale is 0
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
           p0 = (key > qrow) ? 0.f : p0;
           p1 = (key + 1 > qrow) ? 0.f : p1;
@@ -234,20 +244,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         pk[sb][e >> 1] = pack_bf16x2(p0, p1);
       }
 
-    // O^T += V^T P^T over the tile's keys, 16 at a time
+    // O^T += V^T P^T over the tile's keys, 16 at a time; the V^T operands of
+    // one key step are all requested before its products
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int sb = t >> 1, hf = t & 1;
       u32x4 pv = {pk[sb][4 * hf + 0], pk[sb][4 * hf + 1], pk[sb][4 * hf + 2], pk[sb][4 * hf + 3]};
       const bf16x8 pop = __builtin_bit_cast(bf16x8, pv);
+      bf16x8 vop[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const bf16x4 v0 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[0][db]);
         const bf16x4 v1 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[1][db]);
-        const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma32(vop, pop, oacc[db]);
+        vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vop[db], pop, oacc[db]);
     }
+  };
+
+  lds_char* K0 = (lds_char*)k_lds0;
+  lds_char* K1 = (lds_char*)k_lds1;
+  lds_char* V0 = (lds_char*)v_lds0;
+  lds_char* V1 = (lds_char*)v_lds1;
+  issue_tile(0, K0, V0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile_step(kt, K0, V0, K1, V1);
+    if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
   }
 
   if (!wave_active) return;

@@ -95,7 +95,8 @@ def sample_rows(n: int, count: int, rng: np.random.Generator, extra=()) -> np.nd
 # ---------------------------------------------------------------------------
 # Error bounds derived from the arithmetic, for stress cases outside the five
 # workloads (for example much larger softmax scales).  First order in the
-# bfloat16 unit roundoff u = 2^-9 (half an ulp relative), worst case over
+# bfloat16 unit roundoff u = 2^-8 (8 significant bits: half an ulp is at
+# most 2^-8 of the value), worst case over
 # signs:
 #   forward: P rounded to bf16 for the PV product (relative u each) and the
 #     row sum taken from the unrounded P (another u):
@@ -107,7 +108,7 @@ def sample_rows(n: int, count: int, rng: np.random.Generator, extra=()) -> np.nd
 #       dV_jc: u sum_i P_ij |dO_ic|
 # Each bound is added to half an ulp of the bf16 output.
 
-U_BF16 = 2.0 ** -9
+U_BF16 = 2.0 ** -8
 
 
 def _probabilities(q, k, scale, causal):
