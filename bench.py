@@ -250,7 +250,7 @@ def main(argv=None):
             "ms_p90": round(pct(bwd_ms, 0.9), 4), "useful_tflop": round(bf / 1e12, 4),
         },
         "roofline": {
-            "kernel": "fwd_kernel<128,4,64,causal>",
+            "kernel": "fwd_kernel<128,8,64,true> (8 waves, 256 query rows per workgroup, 64-key tiles)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -82,7 +82,11 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.B = B;
   a.H = H;
   a.N = N;
-  a.c = fabsf(scale) * 1.4426950408889634f;
+  // scores enter the kernel as s * c in base 2.  c is kept away from 0: a
+  // masked score (-inf) times c must stay -inf, and with scale == 0 a c of
+  // 1e-30 leaves every finite s * c within 1e-24 of 0, where exp2 rounds to
+  // exactly 1 in float32, as for c = 0.
+  a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);
   a.negate = scale < 0.f;
   const hipError_t e = fa::launch_fwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -31,6 +31,8 @@
 //  * workgroup order: heaviest causal query tiles first, and each XCD
 //    (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
 //    set of heads so the query tiles sharing K and V share an L2.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -169,17 +171,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const float c = a.c;
   const int qrow = qw + l32;
 
-  // one key tile: wait for its copies, start the next tile's copies into
-  // the other buffer, then compute on this one
-  auto tile_step = [&](int kt, const lds_char* kt_lds, const lds_char* vt_lds,
-                       lds_char* knext, lds_char* vnext) {
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
-    const int kb = kt * BC;
-    if (!wave_active) return;
-    if (CAUSAL && kb > qw + 31) return;  // whole tile in this wave's future
-
+  // Work on one key tile held in LDS.  MASK (std::true_type or
+  // std::false_type) selects the variant for tiles crossing this wave's
+  // diagonal; every other tile runs without a single masking instruction.
+  auto compute_tile = [&](auto MASK, int kb, const lds_char* kt_lds, const lds_char* vt_lds) {
+    constexpr bool MASKED = decltype(MASK)::value;
     // S^T (keys x queries) for each 32-key sub-block.  All K operands of a
     // sub-block are requested from LDS before its first product so the
     // reads overlap the matrix-core work instead of each product waiting.
@@ -194,9 +190,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk) sacc[sb] = mfma32(kop[kk], qop[kk], sacc[sb]);
     }
 
-    // causal mask on tiles crossing the diagonal: key > query -> -inf
-    const bool diag = CAUSAL && (kb + BC - 1 > qw);
-    if (diag) {
+    // causal mask on tiles crossing the diagonal: key > query -> -inf.  The
+    // scale factor c is never 0 (the host clamps it to a tiny positive
+    // number), so exp2(-inf * c - m) below is exactly 0 with no second mask.
+    if constexpr (MASKED) {
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -233,13 +230,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
-        float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
-        if (diag) {  // exp2(-inf) is 0 already unless scale is 0
-          const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          p0 = (key > qrow) ? 0.f : p0;
-          p1 = (key + 1 > qrow) ? 0.f : p1;
-        }
+        const float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
+        const float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
         l_run += p0 + p1;
         pk[sb][e >> 1] = pack_bf16x2(p0, p1);
       }
@@ -261,6 +253,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vop[db], pop, oacc[db]);
     }
+  };
+
+  // one key tile: wait for its copies, start the next tile's copies into
+  // the other buffer, then compute on this one
+  auto tile_step = [&](int kt, const lds_char* kt_lds, const lds_char* vt_lds,
+                       lds_char* knext, lds_char* vnext) {
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
+    const int kb = kt * BC;
+    if (!wave_active) return;
+    if (CAUSAL && kb > qw + 31) return;  // whole tile in this wave's future
+    if (CAUSAL && kb + BC - 1 > qw)
+      compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
+    else
+      compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
   };
 
   lds_char* K0 = (lds_char*)k_lds0;
@@ -301,7 +309,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_fwd_t<128, 4, 64, true>(a, stream) : launch_fwd_t<128, 4, 64, false>(a, stream);
+  if (d == 128) return causal ? launch_fwd_t<128, 8, 64, true>(a, stream) : launch_fwd_t<128, 8, 64, false>(a, stream);
   return causal ? launch_fwd_t<64, 4, 64, true>(a, stream) : launch_fwd_t<64, 4, 64, false>(a, stream);
 }
 
