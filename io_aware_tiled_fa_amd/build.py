@@ -30,33 +30,54 @@ def hipcc() -> str:
     return path
 
 
+# per-source device flags
+EXTRA = {
+    # forward: matrix-core accumulators in VGPRs, so the scores feed the
+    # softmax and O is rescaled without AGPR <-> VGPR copies
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # backward: likewise, except the dK / dV accumulators, which are pinned
+    # to AGPRs (only the matrix cores touch them until the epilogue)
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_api.hip": [],
+}
+
+
 def flags() -> list:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from forming packed fp32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # matrix-core accumulators in VGPRs: no AGPR <-> VGPR copies around
-        # the softmax and the rescale of O
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
     ]
 
 
-def build(asm_dir: str | None = None, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
-    if asm_dir:
-        os.makedirs(asm_dir, exist_ok=True)
-        cmd += ["-save-temps", "-Rpass-analysis=kernel-resource-usage"]
-    cwd = asm_dir if asm_dir else None
-    if asm_dir:
-        cmd[cmd.index("-o") + 1] = os.path.abspath(tmp)
+def _run(cmd, cwd=None):
     res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in line)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(asm_dir: str | None = None, verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libfa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.abspath(asm_dir) if asm_dir else os.path.join(ROOT, "_build", "obj")
+    os.makedirs(objdir, exist_ok=True)
+    extra = ["-save-temps", "-Rpass-analysis=kernel-resource-usage"] if asm_dir else []
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc()] + flags() + EXTRA.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+        return obj, _run(cmd, cwd=objdir)
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    out = "\n".join(r[1] for r in results)
+    out += _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [r[0] for r in results] + ["-o", tmp])
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
