@@ -78,9 +78,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this shape: a float32 [B, H, N]
- * row term D_i = sum_c dO_ic * O_ic and a float32 [B, N, H, d] dQ
- * accumulator, each 256-byte aligned.  Returns 0 for an invalid shape.
+ * Bytes of device workspace fa_bwd needs for this shape: two float32
+ * [B, H, N] row terms, D_i = sum_c dO_ic * O_ic and -lse_i * log2(e),
+ * rounded up to a multiple of 256 bytes.  Returns 0 for an invalid shape.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -96,8 +96,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *                bytes, 256-byte aligned, caller-owned; its contents on
  *                entry do not matter and are overwritten.
  * The probabilities are recomputed tile by tile as exp(s_ij - lse_i); the
- * score and probability matrices are never stored.  dQ is accumulated with
- * float32 atomic adds, so its last bits may differ from run to run.
+ * score and probability matrices are never stored.  Every output element is
+ * summed in a fixed order, so results are identical from run to run.
  * Returns FA_OK or an FA_ERR_* code.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,

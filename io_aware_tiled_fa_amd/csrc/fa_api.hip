@@ -95,7 +95,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d) != FA_OK) return 0;
   const size_t rows = (size_t)B * H * N;
-  return round256(2 * rows * sizeof(float)) + round256((size_t)B * N * H * d * sizeof(float));
+  return round256(2 * rows * sizeof(float));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -136,7 +136,6 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.drow = static_cast<float*>(workspace);
-  a.dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(2 * (size_t)B * H * N * sizeof(float)));
   a.B = B;
   a.H = H;
   a.N = N;

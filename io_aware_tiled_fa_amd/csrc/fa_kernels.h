@@ -28,8 +28,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* drow;   // [B, H, N] row term sum_c dO * O
-  float* dqacc;  // [B, N, H, d] float32 dQ accumulator
+  float* drow;   // [B, H, N] row term sum_c dO * O, then [B, H, N] -L log2(e)
   int B, H, N;
   float scale;   // signed softmax scale
   float c;       // scale * log2(e) (signed)

@@ -93,7 +93,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, N=65) == -4
     assert bwd(lib, dk=P[7] + 2) == -5
     assert bwd(lib, ws=None) == -6
-    assert bwd(lib, ws_bytes=1024) == -6
+    assert bwd(lib, ws_bytes=1023) == -6               # one byte short of the 1024 needed
     assert bwd(lib, ws=P[9] + 16) == -6               # workspace must be 256-byte aligned
     assert bwd(lib, scale=float("nan")) == -7
     assert bwd(lib, causal=-1) == -9
@@ -106,10 +106,10 @@ def test_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(0, 1, 64, 64) == 0
     assert lib.fa_bwd_workspace_size(1, 1, 64, 80) == 0
     B, H, N, d = 4, 16, 4096, 128
-    rows = B * H * N * 4 * 2
-    acc = B * N * H * d * 4
+    rows = B * H * N * 4 * 2          # D and -lse * log2(e), float32 each
     r256 = lambda x: (x + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_size(B, H, N, d) == r256(rows) + r256(acc)
+    assert lib.fa_bwd_workspace_size(B, H, N, d) == r256(rows)
+    assert lib.fa_bwd_workspace_size(1, 3, 64, 64) == r256(3 * 64 * 4 * 2)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -76,6 +76,20 @@ def test_backward_scales(fa, scale):
     check_bwd(fa, inp, True, scale, derived_bound=True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_deterministic(fa, d):
+    """Each gradient element is summed in a fixed order (no atomics), so two
+    runs on the same inputs agree bit for bit."""
+    import torch
+
+    announce(f"bwd determinism d={d}")
+    inp = make_inputs(2, 4, 384, d, seed=5, with_do=True)
+    first = run_bwd(fa, inp, True, 1.0 / math.sqrt(d))
+    second = run_bwd(fa, inp, True, 1.0 / math.sqrt(d))
+    for name, x, y in zip(("dQ", "dK", "dV"), first, second):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"{name} differs between runs"
+
+
 def test_workload_bwd_b4_h16_n4096_d128_causal(fa):
     announce("bwd workload B=4 H=16 N=4096 d=128 causal (every element)")
     inp = make_workload("bwd_b4_h16_n4096_d128_causal")
