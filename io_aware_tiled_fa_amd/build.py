@@ -34,10 +34,12 @@ def hipcc() -> str:
 EXTRA = {
     # forward: matrix-core accumulators in VGPRs, so the scores feed the
     # softmax and O is rescaled without AGPR <-> VGPR copies
-    "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    # backward: likewise, except the dK / dV accumulators, which are pinned
-    # to AGPRs (only the matrix cores touch them until the epilogue)
-    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # softmax and O is rescaled without AGPR <-> VGPR copies.  No step of the
+    # kernels relies on NaN semantics (scores are finite or -inf), and without
+    # them a max needs no extra canonicalising instruction per operand.
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    # backward: likewise
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fa_api.hip": [],
 }
 

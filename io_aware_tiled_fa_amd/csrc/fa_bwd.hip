@@ -36,11 +36,19 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+#ifndef PROD_AHEAD
+#define PROD_AHEAD 3
+#endif
+#ifndef CONS_AHEAD
+#define CONS_AHEAD 2
+#endif
+
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. row terms and accumulator clear.  One 16-lane group per (b, n, h) row for
-//    d = 128 (8-lane for d = 64); 256 threads per block.
+// 1. row terms: -D_i = -sum_c dO_ic O_ic and -L_i log2(e), float32.  One
+//    16-lane group per (b, n, h) row for d = 128 (8-lane for d = 64); 256
+//    threads per block.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;            // lanes per row, 8 bf16 each
@@ -70,59 +78,71 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int n = (int)(bn % a.N);
     const int b = (int)(bn / a.N);
     const size_t r = ((size_t)b * a.H + h) * a.N + n;
-    a.drow[r] = acc;
+    a.drow[r] = -acc;
     a.drow[(size_t)a.B * a.H * a.N + r] = -a.lse[r] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. main kernel: one workgroup of 8 waves per 128-key block, walking the
-//    query blocks of 64 rows.  Wave w = kg + 4 dh (waves w and w + 4 share a
-//    SIMD): key group kg owns keys 32 kg .. 32 kg + 31 of the block, and dh
-//    picks both the 32-row query half whose scores the wave computes and the
-//    half of the d columns of dK and dV it accumulates.  Per query block:
-//      S, dP for (key group, query half)       8 + 8 products (k = d)
-//      P, dS -> LDS (bf16, [key][query])
-//      dQ block (query half, 32 columns) = dS K, added atomically
-//      dV, dK (key group, d half) over all 64 queries: the own half's P and
-//      dS from registers, the partner wave's from LDS
-//    With two waves per SIMD, one wave's softmax runs beside the other's
-//    matrix products.
+// 2. dK / dV kernel: one workgroup of 8 waves per 128-key block, walking the
+//    query blocks of 32 rows.  The waves specialise: wave w < 4 produces and
+//    wave w + 4 (on the same SIMD) consumes for key group kg = w, keys
+//    32 kg .. 32 kg + 31 of the block.  In step t:
+//      producer (block t):     S = Q K^T and dP - D = dO V^T - D      16 products
+//                              P = exp2(S c - L log2 e) (masked), dS = P (dP - D)
+//                              P^T, dS^T -> LDS (bf16)
+//      consumer (block t - 1): dV += P^T dO, dK += dS^T Q over its 32 rows     16 products
+//    so the producer's softmax runs beside the consumer's matrix products.
+//    One barrier per step; Q / dO tiles are triple-buffered (the producer
+//    reads block t, the consumer block t - 1, the copies fill block t + 1)
+//    and the P^T / dS^T tiles double-buffered.
 //
-// P^T / dS^T tiles: 128 key rows of 64 queries (128 B), stored in 8-byte
-// chunks of 4 queries with chunk c of row r at c ^ f(r), f(r) = 8 r1 + (r >> 2
-// & 7): conflict-free for the 32-row chunk writes and reads of a key group
-// and for the transpose reads of the dQ product.
+// P^T / dS^T tiles: 128 key rows of 32 queries (64 B), in 8-byte chunks of 4
+// queries, chunk c of row r at c ^ ((r >> 2) & 7): conflict-free for the
+// 32-row chunk writes and reads of a key group.
+template <int I>
+using IC = std::integral_constant<int, I>;
+
 __device__ __forceinline__ int pt_off(int row, int q) {
-  const int f = (((row >> 1) & 1) << 3) | ((row >> 2) & 7);
-  return row * 128 + (((q >> 2) ^ f) << 3) + 2 * (q & 3);
+  return row * 64 + (((q >> 2) ^ ((row >> 2) & 7)) << 3) + 2 * (q & 3);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
-  constexpr int NW = 8;
   constexpr int BC = 128;              // keys per workgroup (4 groups of 32)
-  constexpr int BR = 64;               // queries per step (2 halves of 32)
-  constexpr int ROWB = D * 2;          // bytes per row of a Q / dO / K tile
+  constexpr int BR = 32;               // queries per step
+  constexpr int ROWB = D * 2;          // bytes per row of a Q / dO tile
   constexpr int QTILEB = BR * ROWB;    // Q or dO tile
   constexpr int PTB = BC * BR * 2;     // P^T or dS^T tile
   constexpr int NCH = D / 8;
   constexpr int NKK = D / 16;          // k-steps over d
   constexpr int NDB = D / 32;          // 32-wide column blocks over d
-  constexpr int NDH = NDB / 2;         // column blocks of dK, dV per wave
-  constexpr int QLPW = QTILEB / 1024 / NW;
-  static_assert(QLPW >= 1 && NDH >= 1, "tile copies must split evenly over waves");
+  constexpr int QLPW = 2 * QTILEB / 1024 / 4;  // copies per consumer wave per step (Q and dO)
+  static_assert(QLPW >= 1, "tile copies must split evenly over the waves");
+  // Q / dO tiles and row terms in 4 buffers (the producer's products read
+  // block t + 1, its softmax block t's row terms, the consumer block t - 1,
+  // the copies fill block t + 2); P^T / dS^T in 2.  Every buffer is a
+  // separate object and the walk is unrolled by 4, so every access names its
+  // buffer at compile time: the compiler can then see that the copies into
+  // one buffer never alias the reads of another and does not hold the reads
+  // back until the copies land.
   __shared__ __attribute__((aligned(1024))) char q_lds0[QTILEB];
   __shared__ __attribute__((aligned(1024))) char q_lds1[QTILEB];
+  __shared__ __attribute__((aligned(1024))) char q_lds2[QTILEB];
+  __shared__ __attribute__((aligned(1024))) char q_lds3[QTILEB];
   __shared__ __attribute__((aligned(1024))) char g_lds0[QTILEB];
   __shared__ __attribute__((aligned(1024))) char g_lds1[QTILEB];
-  __shared__ __attribute__((aligned(1024))) char p_lds[PTB];
-  __shared__ __attribute__((aligned(1024))) char ds_lds[PTB];
-  // row terms of a query block: -L log2(e) of its 64 rows, then their D
+  __shared__ __attribute__((aligned(1024))) char g_lds2[QTILEB];
+  __shared__ __attribute__((aligned(1024))) char g_lds3[QTILEB];
+  __shared__ __attribute__((aligned(1024))) char p_lds0[PTB];
+  __shared__ __attribute__((aligned(1024))) char p_lds1[PTB];
+  __shared__ __attribute__((aligned(1024))) char ds_lds0[PTB];
+  __shared__ __attribute__((aligned(1024))) char ds_lds1[PTB];
+  // row terms of a query block: -L log2(e) of its 32 rows, then their -D
   __shared__ __attribute__((aligned(256))) float r_lds0[2 * BR];
   __shared__ __attribute__((aligned(256))) float r_lds1[2 * BR];
-  lds_char* const ptile = (lds_char*)p_lds;
-  lds_char* const dstile = (lds_char*)ds_lds;
+  __shared__ __attribute__((aligned(256))) float r_lds2[2 * BR];
+  __shared__ __attribute__((aligned(256))) float r_lds3[2 * BR];
 
   const int nbh = a.B * a.H;
   const int wg = blockIdx.x;
@@ -141,39 +161,27 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   const int b = bh / a.H, h = bh - b * a.H;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l = threadIdx.x & 63, h2 = l >> 5, l32 = l & 31;
-  const int kg = w & 3, dh = w >> 2;
+  const bool producer = w < 4;
+  const int kg = w & 3;
   const int kb = kblk * BC;
-  const int kw = kb + 32 * kg;  // first key of this wave
+  const int kw = kb + 32 * kg;  // first key of this wave's group
   // N is a multiple of 64, so the last key block may hold only 64 keys:
-  // key groups past the end compute nothing and leave P = dS = 0
-  const bool wave_active = kw < a.N;
+  // key groups past the end compute nothing
+  const bool group_active = kw < a.N;
 
   const size_t rs = (size_t)a.H * D;
   const size_t head_off = (size_t)b * a.N * rs + (size_t)h * D;
   const size_t rowterm_off = ((size_t)b * a.H + h) * a.N;
-  const float* drow = a.drow + rowterm_off;
+  const float* ndrow = a.drow + rowterm_off;
   const float* nlse2 = a.drow + (size_t)a.B * a.H * a.N + rowterm_off;
-
-  // ---- the key group's keys and values as B operands: lane = key l32, d = 16 kk + 8 h2 ..
-  bf16x8 kreg[NKK], vreg[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) kreg[kk] = vreg[kk] = bf16x8{};
-  if (wave_active) {
-    const __bf16* kr = a.k + head_off + (size_t)(kw + l32) * rs + 8 * h2;
-    const __bf16* vr = a.v + head_off + (size_t)(kw + l32) * rs + 8 * h2;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kreg[kk] = *(const bf16x8*)(kr + 16 * kk);
-      vreg[kk] = *(const bf16x8*)(vr + 16 * kk);
-    }
-  }
 
   // ---- per-lane LDS offsets.  Q / dO tiles use the forward kernel's
   // geometry; the swizzle XORs the chunk index, so a power-of-two chunk step
   // is an XOR of the offset.
-  // row reads (A operand, lane = row l32 of the wave's query half, chunk 2 kk + h2)
-  const int roff = dh * 32 * ROWB + l32 * ROWB + ((chunk_swizzle<D>(l32) ^ h2) << 4);
-  // transpose reads: rows 4 h2 + j/4 (+8) of a 16-row step, cols 16 (g&1) + 4 (j&3) of a 32-col block
+  // producer row reads (A operand, lane = row l32, chunk 2 kk + h2) at roff ^ (kk << 5)
+  const int roff = l32 * ROWB + ((chunk_swizzle<D>(l32) ^ h2) << 4);
+  // consumer transpose reads: rows 4 h2 + j/4 (+8) of a 16-row step, columns
+  // 32 db + 16 (g&1) + 4 (j&3), at troff0[r] ^ (db << 6)
   int troff0[2];
   {
     const int g = l >> 4, j = l & 15;
@@ -184,185 +192,255 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
       troff0[r] = row * ROWB + ((ch ^ chunk_swizzle<D>(row)) << 4) + 8 * (j & 1);
     }
   }
-  // P^T / dS^T chunk of this lane: key row 32 kg + l32, queries 32 hf + 8 g4 + 4 h2
-  // at pwbase ^ (64 hf + 16 g4)
-  const int pwbase = pt_off(32 * kg + l32, 4 * h2);
-  // direct copies of a 64-row Q or dO tile
+  // P^T / dS^T chunk of this lane: key row 32 kg + l32, queries 8 g4 + 4 h2 at
+  // pbase ^ (16 g4)
+  const int pbase = pt_off(32 * kg + l32, 4 * h2);
+  // direct copies of a 32-row Q or dO tile, all issued by the consumer waves
+  // (the producers then have no copy in flight that the compiler would make
+  // their LDS writes wait for): copy i of consumer wave w - 4 is 1 KiB slot
+  // w - 4 + 4 i of the pair (Q tile slots first, then dO)
   int qgoff[QLPW];
 #pragma unroll
   for (int i = 0; i < QLPW; ++i) {
-    const int c = w + NW * i;
+    const int c = ((w & 3) + 4 * i) % (QTILEB / 1024);
     const int p = 64 * c + l;
     const int row = p / NCH, ch = p % NCH;
     qgoff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
   }
-  // copies of one query block: the Q and dO tiles (all waves), and its row
-  // terms, 64 + 64 floats in two 4-byte-per-lane copies (wave 0)
-  auto issue_q = [&](int qblk, lds_char* qdst, lds_char* gdst, float* rdst) __attribute__((always_inline)) {
+  // buffer I (a std::integral_constant) of each kind
+  auto QT = [&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value & 3;
+    return (lds_char*)(i == 0 ? q_lds0 : i == 1 ? q_lds1 : i == 2 ? q_lds2 : q_lds3);
+  };
+  auto GT = [&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value & 3;
+    return (lds_char*)(i == 0 ? g_lds0 : i == 1 ? g_lds1 : i == 2 ? g_lds2 : g_lds3);
+  };
+  auto RT = [&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value & 3;
+    return (float*)(i == 0 ? r_lds0 : i == 1 ? r_lds1 : i == 2 ? r_lds2 : r_lds3);
+  };
+  auto PT = [&](auto I) __attribute__((always_inline)) { return (lds_char*)((decltype(I)::value & 1) ? p_lds1 : p_lds0); };
+  auto DT = [&](auto I) __attribute__((always_inline)) { return (lds_char*)((decltype(I)::value & 1) ? ds_lds1 : ds_lds0); };
+  // copies of query block qblk into Q / dO / row-term buffer I
+  auto issue_q = [&](int qblk, auto I) __attribute__((always_inline)) {
     const __bf16* qg = a.q + head_off + (size_t)qblk * BR * rs;
     const __bf16* gg = a.dO + head_off + (size_t)qblk * BR * rs;
+    if (producer) return;
 #pragma unroll
     for (int i = 0; i < QLPW; ++i) {
-      const int c = w + NW * i;
-      copy16_to_lds(qg + qgoff[i], (lds_void*)(qdst + c * 1024));
-      copy16_to_lds(gg + qgoff[i], (lds_void*)(gdst + c * 1024));
+      const int slot = (w & 3) + 4 * i;  // wave-uniform
+      const int c = slot % (QTILEB / 1024);
+      if (slot < QTILEB / 1024)
+        copy16_to_lds(qg + qgoff[i], (lds_void*)(QT(I) + c * 1024));
+      else
+        copy16_to_lds(gg + qgoff[i], (lds_void*)(GT(I) + c * 1024));
     }
-    if (w == 0) {
-      __builtin_amdgcn_global_load_lds(nlse2 + qblk * BR + l, (lds_void*)rdst, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(drow + qblk * BR + l, (lds_void*)(rdst + BR), 4, 0, 0);
+    // the row terms are copied by a consumer wave, so the producers' writes
+    // to the P^T / dS^T tiles never wait behind a copy the compiler cannot
+    // tell apart from them
+    if (w == 4) {  // lanes 0-31: -L log2 e, lanes 32-63: -D of the block's rows
+      const float* src = (l < 32) ? (nlse2 + qblk * BR + l) : (ndrow + qblk * BR + (l - 32));
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)RT(I), 4, 0, 0);
     }
   };
+  auto step_barrier = [&]() __attribute__((always_inline)) {
+    wait_vmem();
+    barrier_lds();
+  };
 
-  f32x16 dvacc[NDH], dkacc[NDH];
-#pragma unroll
-  for (int j = 0; j < NDH; ++j) {
-    dvacc[j] = f32x16{};
-    dkacc[j] = f32x16{};
-  }
   const float c = a.c;
   const int nqb = a.N / BR;
   const int qstart = CAUSAL ? (kb / BR) : 0;
   const int key = kw + l32;
+  const int nsteps = nqb - qstart + 1;
 
-  auto qblock = [&](int qi, const lds_char* __restrict__ qt, const lds_char* __restrict__ gt,
-                    const float* __restrict__ rcur, lds_char* __restrict__ qnext, lds_char* __restrict__ gnext,
-                    float* __restrict__ rnext) __attribute__((always_inline)) {
-    // this block's copies have landed and every wave is done with the
-    // previous block (its P / dS tiles and the buffers about to be refilled)
-    barrier_vmem<0>();
-    if (qi + 1 < nqb) issue_q(qi + 1, qnext, gnext, rnext);
-    const int q0 = qi * BR;
+  // ---- the walk.  Step t produces P^T / dS^T of block qstart + t and
+  // consumes block qstart + t - 1.  The two roles run separate loops (their
+  // registers never live at the same time) with the same barriers: s_barrier
+  // counts arrivals, so every wave passes one per step.
+  issue_q(qstart, IC<0>{});
+  if (qstart + 1 < nqb) issue_q(qstart + 1, IC<1>{});
+  step_barrier();
 
-    // S = Q K^T and dP = dO V^T for the wave's query half; lane holds
-    // [query 32 dh + 8(e/4)+4h2+e%4][key l32].  The operands of k-step kk + 2
-    // are requested before the products of k-step kk (a ring of three).
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    bf16x8 ring[3][2];
-    auto read_rows = [&](int kk, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-      const int off = roff ^ (kk << 5);
-      dst[0] = lds_read16(qt + off);
-      dst[1] = lds_read16(gt + off);
-    };
-    read_rows(0, ring[0]);
-    read_rows(1, ring[1]);
+  if (producer) {
+    // the group's keys and values as B operands (lane = key l32, d = 16 kk + 8 h2 ..)
+    bf16x8 kreg[NKK], vreg[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 2 < NKK) read_rows(kk + 2, ring[(kk + 2) % 3]);
-      __builtin_amdgcn_sched_barrier(0);
-      sacc = mfma32(ring[kk % 3][0], kreg[kk], sacc);
-      pacc = mfma32(ring[kk % 3][1], vreg[kk], pacc);
+    for (int kk = 0; kk < NKK; ++kk) kreg[kk] = vreg[kk] = bf16x8{};
+    if (group_active) {
+      const __bf16* kr = a.k + head_off + (size_t)(kw + l32) * rs + 8 * h2;
+      const __bf16* vr = a.v + head_off + (size_t)(kw + l32) * rs + 8 * h2;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        kreg[kk] = *(const bf16x8*)(kr + 16 * kk);
+        vreg[kk] = *(const bf16x8*)(vr + 16 * kk);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // P = exp2(S c - L log2 e) (masked), dS = P (dP - D); both to bf16
-    const int qh0 = q0 + 32 * dh;
-    const bool diag = CAUSAL && (qh0 < kw + 31);
-    uint32_t ppk[8], dspk[8];
-    {
-      const __attribute__((address_space(3))) f32x4* r4 = (const __attribute__((address_space(3))) f32x4*)rcur;
+    typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
+    // S (lane = key l32, e -> query 8(e/4)+4h2+e%4) and dP - D, the latter
+    // accumulated onto -D, of the block in buffer qb4 / row terms rb3.
+    // Products only; operands of k-step kk + 2 requested before those of kk.
+    // With `soft`, the softmax of the previous block's (sc, pc) into (ppk,
+    // dspk) is spread over the products, one element pair per k-step.
+    auto products = [&](auto I, f32x16& sn, f32x16& pn, auto SOFT, const f32x16& sc, const f32x16& pc,
+                        const float (&nlv)[16], uint32_t (&ppk)[8], uint32_t (&dspk)[8]) __attribute__((always_inline)) {
+      constexpr bool S_ON = decltype(SOFT)::value;
+      const lds_char* qt = QT(I);
+      const lds_char* gt = GT(I);
+      lds_f32x4* r4 = (lds_f32x4*)RT(I);
+      sn = f32x16{};
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 nl = r4[(32 * dh + 8 * g4 + 4 * h2) >> 2];
-        const f32x4 dr = r4[(BR + 32 * dh + 8 * g4 + 4 * h2) >> 2];
+        const f32x4 nd = r4[(BR + 8 * g4 + 4 * h2) >> 2];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; e2 += 2) {
-          const int e = 4 * g4 + e2;
-          float p0 = fast_exp2(fmaf(sacc[e], c, nl[e2]));
-          float p1 = fast_exp2(fmaf(sacc[e + 1], c, nl[e2 + 1]));
-          if (diag) {
-            const int qrow = qh0 + 8 * g4 + 4 * h2 + e2;
-            p0 = (key > qrow) ? 0.f : p0;
-            p1 = (key > qrow + 1) ? 0.f : p1;
+        for (int i = 0; i < 4; ++i) pn[4 * g4 + i] = nd[i];
+      }
+      constexpr int PD = PROD_AHEAD;  // k-steps the operand reads run ahead
+      bf16x8 ring[PD + 1][2];
+      auto read_rows = [&](int kk, bf16x8 (&dst2)[2]) __attribute__((always_inline)) {
+        const int off = roff ^ (kk << 5);
+        dst2[0] = lds_read16(qt + off);
+        dst2[1] = lds_read16(gt + off);
+      };
+#pragma unroll
+      for (int kk = 0; kk < PD && kk < NKK; ++kk) read_rows(kk, ring[kk]);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + PD < NKK) read_rows(kk + PD, ring[(kk + PD) % (PD + 1)]);
+        sn = mfma32(ring[kk % (PD + 1)][0], kreg[kk], sn);
+        pn = mfma32(ring[kk % (PD + 1)][1], vreg[kk], pn);
+        if constexpr (S_ON) {
+#pragma unroll
+          for (int u = kk * 8 / NKK; u < (kk + 1) * 8 / NKK; ++u) {
+            const int e = 2 * u;
+            const float p0 = fast_exp2(fmaf(sc[e], c, nlv[e]));
+            const float p1 = fast_exp2(fmaf(sc[e + 1], c, nlv[e + 1]));
+            ppk[u] = pack_bf16x2(p0, p1);
+            dspk[u] = pack_bf16x2(p0 * pc[e], p1 * pc[e + 1]);
+            // keep the conversions in this k-step (the compiler would
+            // otherwise sink them to their use after the products)
+            asm volatile("" : "+v"(ppk[u]), "+v"(dspk[u]));
           }
-          if (!wave_active) p0 = p1 = 0.f;
-          const float ds0 = p0 * (pacc[e] - dr[e2]);
-          const float ds1 = p1 * (pacc[e + 1] - dr[e2 + 1]);
-          ppk[e >> 1] = pack_bf16x2(p0, p1);
-          dspk[e >> 1] = pack_bf16x2(ds0, ds1);
         }
-      }
-    }
-    // P^T and dS^T chunks -> LDS for the partner wave and the dQ product
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      *(__attribute__((address_space(3))) u32x2*)(ptile + (pwbase ^ (64 * dh + 16 * g4))) = u32x2{ppk[2 * g4], ppk[2 * g4 + 1]};
-      *(__attribute__((address_space(3))) u32x2*)(dstile + (pwbase ^ (64 * dh + 16 * g4))) = u32x2{dspk[2 * g4], dspk[2 * g4 + 1]};
-    }
-    barrier_lds();  // P^T and dS^T tiles complete
-    __builtin_amdgcn_sched_barrier(0);
-
-    // dV += P^T dO and dK += dS^T Q over the 64 queries, four steps of 16:
-    // A = P^T / dS^T (own half from registers, the partner's half from LDS),
-    // B = dO / Q columns of this wave's d half by transpose reads
-    // step st = 2 hf + tq: hf = 0 is the own half (dh), hf = 1 the partner's
-    bf16x8 pa[2], sa[2], go[2][NDH], qo[2][NDH];
-    auto read_dv = [&](int st, bf16x8& pa_, bf16x8& sa_, bf16x8 (&go_)[NDH], bf16x8 (&qo_)[NDH])
-        __attribute__((always_inline)) {
-      const int hf = st >> 1, tq = st & 1;
-      if (hf == 0) {
-        pa_ = __builtin_bit_cast(bf16x8, u32x4{ppk[4 * tq], ppk[4 * tq + 1], ppk[4 * tq + 2], ppk[4 * tq + 3]});
-        sa_ = __builtin_bit_cast(bf16x8, u32x4{dspk[4 * tq], dspk[4 * tq + 1], dspk[4 * tq + 2], dspk[4 * tq + 3]});
-      } else {
-        typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-        const int o0 = pwbase ^ (64 * (1 - dh) + 32 * tq);
-        const int o1 = pwbase ^ (64 * (1 - dh) + 32 * tq + 16);
-        const u32x2 p0 = *(const lds_u32x2*)(ptile + o0);
-        const u32x2 p1 = *(const lds_u32x2*)(ptile + o1);
-        const u32x2 s0 = *(const lds_u32x2*)(dstile + o0);
-        const u32x2 s1 = *(const lds_u32x2*)(dstile + o1);
-        pa_ = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
-        sa_ = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
-      }
-      const int qrow16 = 32 * (hf == 0 ? dh : 1 - dh) + 16 * tq;
-#pragma unroll
-      for (int j = 0; j < NDH; ++j) {
-        const int db = dh * NDH + j;
-        const int o0 = qrow16 * ROWB + (troff0[0] ^ (db << 6));
-        const int o1 = qrow16 * ROWB + (troff0[1] ^ (db << 6));
-        go_[j] = __builtin_shufflevector(lds_read_tr16(gt + o0), lds_read_tr16(gt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
-        qo_[j] = __builtin_shufflevector(lds_read_tr16(qt + o0), lds_read_tr16(qt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    read_dv(0, pa[0], sa[0], go[0], qo[0]);
+    f32x16 sA, pA, sB, pB;
+    float nlv[16];
+    uint32_t ppk[8], dspk[8];
+    // step t's softmax uses the scores in (sA, pA) for even t, (sB, pB) for odd
+    // step t = T (mod 4)
+    auto pstep = [&](auto T, int t, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T)::value;
+      const int qi = qstart + t;
+      step_barrier();
+      if (qi + 2 < nqb) issue_q(qi + 2, IC<T4 + 2>{});
+      if (!group_active || qi >= nqb) return;
+      // exp2 addends: -L log2 e of each element's row, -inf where key > query
+      lds_f32x4* r4 = (lds_f32x4*)RT(T);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (st + 1 < 4) read_dv(st + 1, pa[(st + 1) & 1], sa[(st + 1) & 1], go[(st + 1) & 1], qo[(st + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nl = r4[(8 * g4 + 4 * h2) >> 2];
 #pragma unroll
-      for (int j = 0; j < NDH; ++j) {
-        dvacc[j] = mfma32(pa[st & 1], go[st & 1][j], dvacc[j]);
-        dkacc[j] = mfma32(sa[st & 1], qo[st & 1][j], dkacc[j]);
+        for (int i = 0; i < 4; ++i) nlv[4 * g4 + i] = nl[i];
       }
+      const int q0 = qi * BR;
+      if (CAUSAL && q0 < kw + 31) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          nlv[e] = (key > q0 + 8 * (e >> 2) + 4 * h2 + (e & 3)) ? -__builtin_inff() : nlv[e];
+      }
+      // block qi + 1's products beside block qi's softmax (the products of
+      // the block past the end read a stale buffer and are never used)
+      products(IC<T4 + 1>{}, sn, pn, std::true_type{}, sc, pc, nlv, ppk, dspk);
+      // P^T and dS^T chunks -> LDS for the consumer of this key group
+      typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+      lds_char* pt = PT(T);
+      lds_char* dt = DT(T);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        *(lds_u32x2*)(pt + (pbase ^ (16 * g4))) = u32x2{ppk[2 * g4], ppk[2 * g4 + 1]};
+        *(lds_u32x2*)(dt + (pbase ^ (16 * g4))) = u32x2{dspk[2 * g4], dspk[2 * g4 + 1]};
+      }
+    };
+    if (group_active) products(IC<0>{}, sA, pA, std::false_type{}, sB, pB, nlv, ppk, dspk);
+    for (int t = 0; t < nsteps; t += 4) {
+      pstep(IC<0>{}, t, sA, pA, sB, pB);
+      if (t + 1 < nsteps) pstep(IC<1>{}, t + 1, sB, pB, sA, pA);
+      if (t + 2 < nsteps) pstep(IC<2>{}, t + 2, sA, pA, sB, pB);
+      if (t + 3 < nsteps) pstep(IC<3>{}, t + 3, sB, pB, sA, pA);
     }
-  };
-
-  lds_char* const Q0 = (lds_char*)q_lds0;
-  lds_char* const Q1 = (lds_char*)q_lds1;
-  lds_char* const G0 = (lds_char*)g_lds0;
-  lds_char* const G1 = (lds_char*)g_lds1;
-  float* const R0 = r_lds0;
-  float* const R1 = r_lds1;
-  issue_q(qstart, Q0, G0, R0);
-  // the buffer roles alternate; __restrict__ tells the compiler that the
-  // copies into the other buffers do not alias this block's reads
-  for (int qi = qstart; qi < nqb; ++qi) {
-    const bool odd = (qi - qstart) & 1;
-    qblock(qi, odd ? Q1 : Q0, odd ? G1 : G0, odd ? R1 : R0, odd ? Q0 : Q1, odd ? G0 : G1, odd ? R0 : R1);
+    return;
   }
 
-  // ---- dK = scale * dK_acc, dV = dV_acc; lane holds [key kw + 8(e/4)+4h2+e%4][d = 32 db + l32]
-  if (!wave_active) return;
+  // ---- consumer: dV^T += dO^T P and dK^T += Q^T dS over the block's rows,
+  // two steps of 16 queries; lane holds [key 8(e/4)+4h2+e%4][d = 32 db + l32]
+  f32x16 dvacc[NDB], dkacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dvacc[db] = dkacc[db] = f32x16{};
+  auto consume = [&](int qi, const lds_char* __restrict__ qt, const lds_char* __restrict__ gt,
+                     const lds_char* __restrict__ pt, const lds_char* __restrict__ dst)
+      __attribute__((always_inline)) {
+    if (CAUSAL && qi * BR + BR - 1 < kw) return;  // P = dS = 0 for this block
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    // product i = (tq, db): A = P^T / dS^T chunks of the 16 queries of step
+    // tq (queries 16 tq + 4 h2 + 0..3 and + 8), B = dO / Q columns by
+    // transpose reads; operands one product ahead
+    constexpr int NP = 2 * NDB;
+    constexpr int CD = CONS_AHEAD;  // products the operand reads run ahead
+    bf16x8 pa[2], sa[2], go[CD + 1], qo[CD + 1];
+    auto read_op = [&](int i) __attribute__((always_inline)) {
+      const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
+      if (db == 0) {
+        const int o0 = pbase ^ (32 * tq), o1 = pbase ^ (32 * tq + 16);
+        const u32x2 p0 = *(const lds_u32x2*)(pt + o0), p1 = *(const lds_u32x2*)(pt + o1);
+        const u32x2 s0 = *(const lds_u32x2*)(dst + o0), s1 = *(const lds_u32x2*)(dst + o1);
+        pa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
+        sa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+      }
+      const int o0 = 16 * tq * ROWB + (troff0[0] ^ (db << 6));
+      const int o1 = 16 * tq * ROWB + (troff0[1] ^ (db << 6));
+      go[s] = __builtin_shufflevector(lds_read_tr16(gt + o0), lds_read_tr16(gt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+      qo[s] = __builtin_shufflevector(lds_read_tr16(qt + o0), lds_read_tr16(qt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+#pragma unroll
+    for (int i = 0; i < CD && i < NP; ++i) read_op(i);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + CD < NP) read_op(i + CD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
+      dvacc[db] = mfma32(pa[tq & 1], go[s], dvacc[db]);
+      dkacc[db] = mfma32(sa[tq & 1], qo[s], dkacc[db]);
+    }
+  };
+  auto cstep = [&](auto T, int t) __attribute__((always_inline)) {
+    constexpr int T4 = decltype(T)::value;
+    step_barrier();
+    const int qi = qstart + t;
+    if (qi + 2 < nqb) issue_q(qi + 2, IC<T4 + 2>{});
+    if (group_active && t > 0) consume(qi - 1, QT(IC<T4 + 3>{}), GT(IC<T4 + 3>{}), PT(IC<T4 + 1>{}), DT(IC<T4 + 1>{}));
+  };
+  for (int t = 0; t < nsteps; t += 4) {
+    cstep(IC<0>{}, t);
+    if (t + 1 < nsteps) cstep(IC<1>{}, t + 1);
+    if (t + 2 < nsteps) cstep(IC<2>{}, t + 2);
+    if (t + 3 < nsteps) cstep(IC<3>{}, t + 3);
+  }
+
+  // ---- consumer epilogue: dK = scale dK_acc, dV = dV_acc
+  if (!group_active) return;
   const float scale = a.scale;
 #pragma unroll
-  for (int j = 0; j < NDH; ++j)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kr = kw + 8 * (e >> 2) + 4 * h2 + (e & 3);
-      const size_t off = head_off + (size_t)kr * rs + 32 * (dh * NDH + j) + l32;
-      a.dk[off] = (__bf16)(dkacc[j][e] * scale);
-      a.dv[off] = (__bf16)(dvacc[j][e]);
+      const size_t off = head_off + (size_t)kr * rs + 32 * db + l32;
+      a.dk[off] = (__bf16)(dkacc[db][e] * scale);
+      a.dv[off] = (__bf16)(dvacc[db][e]);
     }
 }
 
@@ -423,7 +501,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..), row terms
   bf16x8 qop[NKK], gop[NKK];
-  float nl = 0.f, dr = 0.f;
+  float nl = 0.f, ndr = 0.f;  // -L log2(e) and -D of this lane's row
   if (wave_active) {
     const __bf16* qr = a.q + head_off + (size_t)qrow * rs + 8 * h2;
     const __bf16* gr = a.dO + head_off + (size_t)qrow * rs + 8 * h2;
@@ -433,7 +511,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       gop[kk] = *(const bf16x8*)(gr + 16 * kk);
     }
     const size_t r = ((size_t)b * a.H + h) * a.N + qrow;
-    dr = a.drow[r];
+    ndr = a.drow[r];
     nl = a.drow[(size_t)a.B * a.H * a.N + r];
   } else {
 #pragma unroll
@@ -517,7 +595,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
           p0 = (key > qrow) ? 0.f : p0;
           p1 = (key + 1 > qrow) ? 0.f : p1;
         }
-        dspk[e >> 1] = pack_bf16x2(p0 * (pacc[e] - dr), p1 * (pacc[e + 1] - dr));
+        dspk[e >> 1] = pack_bf16x2(p0 * (pacc[e] + ndr), p1 * (pacc[e + 1] + ndr));
       }
       // dQ^T += K^T dS^T over the sub-block's 32 keys, two steps of 16
 #pragma unroll
