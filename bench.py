@@ -73,6 +73,61 @@ def read_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+HBM_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/hbm_fetch -o p -- "
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/hbm_write -o p -- "
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --hbm-summary gpurun_out/hbm_fetch gpurun_out/hbm_write",
+]
+
+
+def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
+    """Turn the two rocprofv3 counter runs of HBM_COMMANDS into HBM bytes per
+    launch of the forward kernel on the long-context batch.  Each counter is
+    scaled by what it reads for a plain 1 GiB device copy in the same run
+    (the copy moves exactly 1 GiB each way)."""
+    import csv
+    import glob
+
+    fwd_threads = FWD["B"] * FWD["H"] * (FWD["N"] // 256) * 512
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        fwd = [float(r["Counter_Value"]) for r in rows
+               if "fwd_kernel<128" in r["Kernel_Name"] and int(r["Grid_Size"]) == fwd_threads]
+        copy = [float(r["Counter_Value"]) for r in rows if "fa::" not in r["Kernel_Name"]
+                and float(r["Counter_Value"]) > 2 ** 18]  # the 1 GiB copies (KiB units)
+        if not fwd or not copy:
+            raise SystemExit(f"{d}: no {counter} rows for the forward kernel or the copy")
+        return sum(fwd) / len(fwd), sum(copy) / len(copy), len(fwd), len(copy)
+
+    f_kib, f_copy, nf, ncf = read(fetch_dir, "FETCH_SIZE")
+    w_kib, w_copy, nw, ncw = read(write_dir, "WRITE_SIZE")
+    gib_kib = 2.0 ** 20
+    f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
+    rd, wr = f_kib * f_scale * 1024, w_kib * w_scale * 1024
+    return {
+        "kernel": "fwd_kernel<128,8,64,true>",
+        "workload": FWD["name"],
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_launch_raw": round(f_kib, 1),
+        "write_kib_per_launch_raw": round(w_kib, 1),
+        "copy_1gib_fetch_kib_raw": round(f_copy, 1),
+        "copy_1gib_write_kib_raw": round(w_copy, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "hbm_read_bytes_per_launch": round(rd),
+        "hbm_write_bytes_per_launch": round(wr),
+        "hbm_bytes_per_launch": round(rd + wr),
+        "algorithmic_bytes_per_launch": fwd_algorithmic_bytes(FWD),
+        "launches": {"fetch": nf, "write": nw, "copy_fetch": ncf, "copy_write": ncw},
+        "commands": HBM_COMMANDS,
+    }
+
+
 def device_tensor(bits, device):
     import numpy as np
     import torch
@@ -138,7 +193,17 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the forward kernel's HBM counter summary from two rocprofv3 runs")
     args = ap.parse_args(argv)
+
+    if args.hbm_summary:
+        rec = hbm_summary(*args.hbm_summary)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this attention path runs on ONE GPU only (asked for {args.gpus}); "
