@@ -199,14 +199,21 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // (the producers then have no copy in flight that the compiler would make
   // their LDS writes wait for): copy i of consumer wave w - 4 is 1 KiB slot
   // w - 4 + 4 i of the pair (Q tile slots first, then dO)
-  int qgoff[QLPW];
+  // (byte offsets from the tile's first row, one unsigned 32-bit value per
+  // copy, into buffer resources over this head's Q and dO rows)
+  uint32_t qgoff[QLPW];
 #pragma unroll
   for (int i = 0; i < QLPW; ++i) {
     const int c = ((w & 3) + 4 * i) % (QTILEB / 1024);
     const int p = 64 * c + l;
     const int row = p / NCH, ch = p % NCH;
-    qgoff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
+    qgoff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
+  // rows 0 .. N - 1 at a stride of H d, the last ending H d - h d elements
+  // before the end of the head's span; under 2^32 bytes since B N H d < 2^31
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
+  const buf_rsrc qrs = make_rsrc(a.q + head_off, head_bytes);
+  const buf_rsrc grs = make_rsrc(a.dO + head_off, head_bytes);
   // buffer I (a std::integral_constant) of each kind
   auto QT = [&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value & 3;
@@ -224,17 +231,16 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   auto DT = [&](auto I) __attribute__((always_inline)) { return (lds_char*)((decltype(I)::value & 1) ? ds_lds1 : ds_lds0); };
   // copies of query block qblk into Q / dO / row-term buffer I
   auto issue_q = [&](int qblk, auto I) __attribute__((always_inline)) {
-    const __bf16* qg = a.q + head_off + (size_t)qblk * BR * rs;
-    const __bf16* gg = a.dO + head_off + (size_t)qblk * BR * rs;
     if (producer) return;
+    const uint32_t soff = (uint32_t)qblk * (uint32_t)(BR * rs * 2);
 #pragma unroll
     for (int i = 0; i < QLPW; ++i) {
       const int slot = (w & 3) + 4 * i;  // wave-uniform
       const int c = slot % (QTILEB / 1024);
       if (slot < QTILEB / 1024)
-        copy16_to_lds(qg + qgoff[i], (lds_void*)(QT(I) + c * 1024));
+        copy16_to_lds_buf(qrs, qgoff[i], soff, (lds_void*)(QT(I) + c * 1024));
       else
-        copy16_to_lds(gg + qgoff[i], (lds_void*)(GT(I) + c * 1024));
+        copy16_to_lds_buf(grs, qgoff[i], soff, (lds_void*)(GT(I) + c * 1024));
     }
     // the row terms are copied by a consumer wave, so the producers' writes
     // to the P^T / dS^T tiles never wait behind a copy the compiler cannot
@@ -532,21 +538,25 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       troff0[r] = row * ROWB + ((ch ^ chunk_swizzle<D>(row)) << 4) + 8 * (j & 1);
     }
   }
-  int goff[LPW];
+  // (byte offsets, one unsigned 32-bit value per copy, into buffer resources
+  // over this head's K and V rows, sized as in the forward kernel)
+  uint32_t goff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int p = 64 * (w + NW * i) + l;
     const int row = p / NCH, ch = p % NCH;
-    goff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
+    goff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
+  const buf_rsrc krs = make_rsrc(kbase, head_bytes);
+  const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const __bf16* kg = kbase + (size_t)kt * BC * rs;
-    const __bf16* vg = vbase + (size_t)kt * BC * rs;
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds(kg + goff[i], (lds_void*)(kdst + c * 1024));
-      copy16_to_lds(vg + goff[i], (lds_void*)(vdst + c * 1024));
+      copy16_to_lds_buf(krs, goff[i], soff, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(vrs, goff[i], soff, (lds_void*)(vdst + c * 1024));
     }
   };
 

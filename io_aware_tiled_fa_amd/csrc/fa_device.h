@@ -81,6 +81,21 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, lds_void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw, untyped: the fourth
+// descriptor word of the gfx9 family).  Accesses past `bytes` read zero.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte asynchronous copy global -> LDS through a buffer resource: lane l
+// writes bytes [lds + 16 l, lds + 16 l + 16) from byte voff + soff of the
+// buffer (voff per lane, soff wave-uniform).  Unlike copy16_to_lds this
+// needs one VGPR per copy instead of a 64-bit address.
+__device__ __forceinline__ void copy16_to_lds_buf(buf_rsrc r, uint32_t voff, uint32_t soff, lds_void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+
 // wait until every outstanding vector-memory load of this wave has landed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -137,21 +137,27 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // direct HBM -> LDS copies: wave copy c = w + NW i fills LDS bytes
   // [1024 c, 1024 c + 1024) of a tile; lane l fills 16-byte slot 64 c + l,
   // i.e. tile row p / NCH, swizzled chunk p % NCH.
-  int goff[LPW];
+  // (byte offsets from the tile's first row, one unsigned 32-bit value per copy)
+  uint32_t goff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int p = 64 * (w + NW * i) + l;
     const int row = p / NCH, ch = p % NCH;
-    goff[i] = row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3);
+    goff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
-  auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) {
-    const __bf16* kg = kbase + (size_t)kt * BC * rs;
-    const __bf16* vg = vbase + (size_t)kt * BC * rs;
+  // K and V of this (batch, head) as buffer resources: rows 0 .. N - 1 at a
+  // stride of H d elements, the last ending H d - h d elements before the
+  // end of the head's span; under 2^32 bytes since B N H d < 2^31
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
+  const buf_rsrc krs = make_rsrc(kbase, head_bytes);
+  const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
+  auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds(kg + goff[i], (lds_void*)(kdst + c * 1024));
-      copy16_to_lds(vg + goff[i], (lds_void*)(vdst + c * 1024));
+      copy16_to_lds_buf(krs, goff[i], soff, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(vrs, goff[i], soff, (lds_void*)(vdst + c * 1024));
     }
   };
 
