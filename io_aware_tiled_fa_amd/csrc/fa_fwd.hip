@@ -38,11 +38,14 @@
 
 namespace fa {
 
-template <int D, int NW, int BC, bool CAUSAL>
+// LT keys are copied per barrier, computed as LT / BC tiles of BC keys.
+template <int D, int NW, int BC, int LT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
-  constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
+  constexpr int TILEB = LT * ROWB;       // bytes of one K or V load tile
+  constexpr int SUB = LT / BC;           // compute tiles per load tile
+  static_assert(SUB * BC == LT, "load tile must hold whole compute tiles");
   constexpr int NCH = D / 8;             // 16-byte chunks per row
   constexpr int LOADS = TILEB / 1024;    // 1 KiB wave copies per tile
   constexpr int LPW = LOADS / NW;        // copies per wave per tile
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
   const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(LT * rs * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
@@ -162,11 +165,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
 
   // ---- key tiles this workgroup visits
-  const int ntiles_all = a.N / BC;
+  const int ntiles_all = (a.N + LT - 1) / LT;
   int ntiles = ntiles_all;
   if (CAUSAL) {
     const int last_row = min(q0 + BR, a.N) - 1;
-    ntiles = min(ntiles_all, last_row / BC + 1);
+    ntiles = min(ntiles_all, last_row / LT + 1);
   }
 
   f32x16 oacc[NDB];
@@ -268,13 +271,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
-    const int kb = kt * BC;
     if (!wave_active) return;
-    if (CAUSAL && kb > qw + 31) return;  // whole tile in this wave's future
-    if (CAUSAL && kb + BC - 1 > qw)
-      compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
-    else
-      compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int kb = kt * LT + sub * BC;
+      // past the keys (the load tile's copy read zeros there), or whole
+      // tile in this wave's future
+      if (kb >= a.N || (CAUSAL && kb > qw + 31)) return;
+      const lds_char* ks = kt_lds + sub * BC * ROWB;
+      const lds_char* vs = vt_lds + sub * BC * ROWB;
+      if (CAUSAL && kb + BC - 1 > qw)
+        compute_tile(std::true_type{}, kb, ks, vs);
+      else
+        compute_tile(std::false_type{}, kb, ks, vs);
+    }
   };
 
   lds_char* K0 = (lds_char*)k_lds0;
@@ -304,19 +314,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   if (h2 == 0) a.lse[((size_t)b * a.H + h) * a.N + qrow] = (m_run + fast_log2(lt)) * kLn2;
 }
 
-template <int D, int NW, int BC, bool CAUSAL>
+template <int D, int NW, int BC, int LT, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32;
   const int nqb = (a.N + BR - 1) / BR;
   dim3 grid((unsigned)(a.B * a.H * nqb));
   dim3 block(NW * 64);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, CAUSAL>, grid, block, args, 0, stream);
+  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, LT, CAUSAL>, grid, block, args, 0, stream);
 }
 
+// keys copied per barrier (64: measured faster than 128 or 256 at both d)
+#ifndef FWD_LT128
+#define FWD_LT128 64
+#endif
+#ifndef FWD_LT64
+#define FWD_LT64 64
+#endif
+
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_fwd_t<128, 8, 64, true>(a, stream) : launch_fwd_t<128, 8, 64, false>(a, stream);
-  return causal ? launch_fwd_t<64, 4, 64, true>(a, stream) : launch_fwd_t<64, 4, 64, false>(a, stream);
+  if (d == 128)
+    return causal ? launch_fwd_t<128, 8, 64, FWD_LT128, true>(a, stream) : launch_fwd_t<128, 8, 64, FWD_LT128, false>(a, stream);
+  return causal ? launch_fwd_t<64, 4, 64, FWD_LT64, true>(a, stream) : launch_fwd_t<64, 4, 64, FWD_LT64, false>(a, stream);
 }
 
 }  // namespace fa
