@@ -24,13 +24,19 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are caller-owned DEVICE memory.  bf16 tensors are contiguous
- *    [B, N, H, d] (BSHD) with element (b, n, h, c) at ((b*N + n)*H + h)*d + c.
- *    The log-sum-exp is contiguous float32 [B, H, N].
+ *    [B, N, H, d] (BSHD) with element (b, n, h, c) at ((b*N + n)*H + h)*d + c,
+ *    where N is N_q for Q, O, dO, dQ and N_k for K, V, dK, dV (N_q = N_k = N
+ *    for the entry points without the _qk suffix).  The log-sum-exp is
+ *    contiguous float32 [B, H, N_q].
  *  - Base pointers must be 16-byte aligned.  Outputs must not alias inputs.
- *  - d must be 64 or 128.  N must be a positive multiple of 64 (tile size of
- *    the kernels).  B, H >= 1, and B*N*H*d must fit in 2^31 - 1 elements.
+ *  - d must be 64 or 128.  B, H, N_q, N_k >= 1 (any length: the kernels
+ *    mask ragged tiles), and each tensor must have fewer than 2^31 elements.
  *  - scale is any finite float (0 allowed; negative allowed).
- *  - causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *  - causal: 0 = every key visible; 1 = key j visible to query i iff
+ *    j <= i + (N_k - N_q), i.e. the keys are aligned to the end of the
+ *    queries (for N_q = N_k: j <= i).  When N_q > N_k the first N_q - N_k
+ *    query rows see no key: their output row is 0, their log-sum-exp is
+ *    -inf, and their dQ row is 0.
  *  - stream is a hipStream_t (NULL = the legacy default stream).  Calls only
  *    enqueue work and return; results are valid once the stream is
  *    synchronised.  The library allocates no memory and keeps no state
@@ -51,9 +57,9 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
-  FA_ERR_SHAPE = -2,      /* B, H or N not positive, or the size overflows   */
+  FA_ERR_SHAPE = -2,      /* B, H, N_q or N_k not positive, or size overflow */
   FA_ERR_HEADDIM = -3,    /* d is not 64 or 128                              */
-  FA_ERR_SEQLEN = -4,     /* N is not a multiple of the 64-row tile          */
+  FA_ERR_SEQLEN = -4,     /* reserved: every length >= 1 is accepted          */
   FA_ERR_ALIGN = -5,      /* a base pointer is not 16-byte aligned           */
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required         */
   FA_ERR_SCALE = -7,      /* scale is NaN or infinite                        */
@@ -78,9 +84,19 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Forward pass with N_q query rows and N_k key / value rows (cross attention
+ * when they differ; the causal mask is aligned to the end, see above).
+ * q, o: [B, N_q, H, d]; k, v: [B, N_k, H, d]; lse: [B, H, N_q].  Otherwise
+ * as fa_fwd, which is fa_fwd_qk with N_q = N_k = N.
+ */
+fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for this shape: two float32
- * [B, H, N] row terms, D_i = sum_c dO_ic * O_ic and -lse_i * log2(e),
- * rounded up to a multiple of 256 bytes.  Returns 0 for an invalid shape.
+ * [B, H, N] row terms, -D_i = -sum_c dO_ic * O_ic and -lse_i * log2(e),
+ * rounded up to a multiple of 256 bytes.  For fa_bwd_qk pass N = N_q.
+ * Returns 0 for an invalid shape.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -104,6 +120,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  int B, int H, int N, int d, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass with N_q query rows and N_k key / value rows.  q, o, dO, dq:
+ * [B, N_q, H, d]; k, v, dk, dv: [B, N_k, H, d]; lse: [B, H, N_q] from
+ * fa_fwd_qk with the same arguments; workspace of at least
+ * fa_bwd_workspace_size(B, H, N_q, d) bytes.  Keys that no query sees get
+ * dK = dV = 0.  Otherwise as fa_bwd, which is fa_bwd_qk with N_q = N_k = N.
+ */
+fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status s);

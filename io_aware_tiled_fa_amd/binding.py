@@ -26,7 +26,8 @@ FA_STATUS = {
     -4: "FA_ERR_SEQLEN", -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE",
     -7: "FA_ERR_SCALE", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_bwd", "fa_bwd_qk", "fa_bwd_workspace_size", "fa_status_string",
+            "fa_version")
 
 _lib = None
 
@@ -51,6 +52,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_qk.restype = i
+    lib.fa_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_qk.restype = i
+    lib.fa_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -89,8 +94,6 @@ def validate_attention_inputs(q, k, v) -> None:
         raise ValueError(f"Key/Value sequence length mismatch: K={k.shape[1]}, V={v.shape[1]}")
     if not (q.shape[3] == k.shape[3] == v.shape[3]):
         raise ValueError(f"Head dimension mismatch: Q={q.shape[3]}, K={k.shape[3]}, V={v.shape[3]}")
-    if q.shape[1] != k.shape[1]:
-        raise ValueError(f"Query and key lengths must match: Q={q.shape[1]}, K={k.shape[1]}")
     if not (q.device == k.device == v.device):
         raise ValueError("Q, K and V must be on one device")
 
@@ -110,21 +113,23 @@ def default_scale(head_dim: int) -> float:
 
 def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
             out=None, lse=None, stream=None) -> Tuple[object, object]:
-    """O, LSE = fa_fwd(Q, K, V); tensors bf16 [B, N, H, d] on the GPU."""
+    """O, LSE = fa_fwd_qk(Q, K, V); Q bf16 [B, N_q, H, d], K and V bf16
+    [B, N_k, H, d] on the GPU (N_q = N_k is plain self-attention)."""
     import torch
 
     validate_attention_inputs(q, k, v)
-    B, N, H, d = q.shape
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
     if scale is None:
         scale = default_scale(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     lib = load_library()
-    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device, stream))
-    _check(lib, "fa_fwd", st)
+    st = lib.fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream_ptr(q.device, stream))
+    _check(lib, "fa_fwd_qk", st)
     return out, lse
 
 
@@ -134,7 +139,7 @@ def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
              dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV = fa_bwd(...); O and LSE are the forward's outputs."""
+    """dQ, dK, dV = fa_bwd_qk(...); O and LSE are the forward's outputs."""
     import torch
 
     validate_attention_inputs(q, k, v)
@@ -142,8 +147,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
         if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like Q")
     B, N, H, d = q.shape
+    Nk = k.shape[1]
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("LSE must be a contiguous float32 [B, H, N] tensor")
+        raise ValueError("LSE must be a contiguous float32 [B, H, N_q] tensor")
     if scale is None:
         scale = default_scale(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -153,10 +159,10 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     need = int(lib.fa_bwd_workspace_size(B, H, N, d))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    B, H, N, d, float(scale), int(bool(causal)),
-                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                    _stream_ptr(q.device, stream))
-    _check(lib, "fa_bwd", st)
+    st = lib.fa_bwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       B, H, N, Nk, d, float(scale), int(bool(causal)),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       _stream_ptr(q.device, stream))
+    _check(lib, "fa_bwd_qk", st)
     return dq, dk, dv

@@ -4,8 +4,9 @@
 // Shape checks mirror the ones the holysheep.ai review prints for its
 // interface ("Common Errors and Fixes", Error 4: four-dimensional
 // [batch, seq_len, num_heads, head_dim] tensors with matching batch, heads
-// and head_dim, and equal K / V lengths); here every tensor has one shape,
-// so they reduce to positive B, H, N and a supported d.  The same page
+// and head_dim, and equal K / V lengths, while the query length may differ);
+// here Q, O, dO share one shape and K, V another, so they reduce to positive
+// B, H, N_q, N_k and a supported d.  The same page
 // ("Common Errors and Fixes", Error 1) notes that a launch fails when a
 // tile exceeds device limits; here unsupported sizes are refused before
 // anything is launched.
@@ -17,8 +18,6 @@
 
 namespace {
 
-constexpr int kTile = 64;
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -26,12 +25,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-fa_status check_shape(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
+// Sizes: B, H, N_q, N_k >= 1, d in {64, 128}, and every tensor under 2^31
+// elements (the kernels index in 32-bit element offsets within a tensor).
+fa_status check_shape(int B, int H, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  const long long elems = (long long)B * N * H * d;
-  if (elems > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
-  if (N % kTile != 0) return FA_ERR_SEQLEN;
+  if ((long long)B * Nq * H * d > 0x7FFFFFFFLL || (long long)B * Nk * H * d > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -45,9 +44,9 @@ const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H and N must be positive and B*N*H*d must fit in 2^31-1";
+    case FA_ERR_SHAPE: return "B, H, N_q and N_k must be positive and every tensor must have fewer than 2^31 elements";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
-    case FA_ERR_SEQLEN: return "sequence length N must be a multiple of 64";
+    case FA_ERR_SEQLEN: return "sequence length not supported";
     case FA_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_SCALE: return "scale must be a finite float";
@@ -57,21 +56,22 @@ const char* fa_status_string(fa_status s) {
   return "unknown status";
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int H, int N, int d, float scale, int causal, void* stream) {
+fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, N, d);
+  fa_status st = check_shape(B, H, Nq, Nk, d);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  const size_t tb = (size_t)B * N * H * d * 2, lb = (size_t)B * H * N * 4;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * H * d * 2, lb = (size_t)B * H * Nq * 4;
   const void* ins[3] = {q, k, v};
-  for (const void* in : ins)
-    if (overlaps(o, tb, in, tb) || overlaps(lse, lb, in, tb)) return FA_ERR_ARG;
-  if (overlaps(o, tb, lse, lb)) return FA_ERR_ARG;
+  const size_t insz[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(o, qb, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i])) return FA_ERR_ARG;
+  if (overlaps(o, qb, lse, lb)) return FA_ERR_ARG;
 
   fa::FwdArgs a;
   a.q = static_cast<const __bf16*>(q);
@@ -81,7 +81,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.lse = lse;
   a.B = B;
   a.H = H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
   // scores enter the kernel as s * c in base 2.  c is kept away from 0: a
   // masked score (-inf) times c must stay -inf, and with scale == 0 a c of
   // 1e-30 leaves every finite s * c within 1e-24 of 0, where exp2 rounds to
@@ -92,32 +93,36 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
-  if (check_shape(B, H, N, d) != FA_OK) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return round256(2 * rows * sizeof(float));
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream) {
+  return fa_fwd_qk(q, k, v, o, lse, B, H, N, N, d, scale, causal, stream);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                 int B, int H, int N, int d, float scale, int causal,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, 1, d) != FA_OK) return 0;
+  return round256(2 * (size_t)B * H * N * sizeof(float));
+}
+
+fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, N, d);
+  fa_status st = check_shape(B, H, Nq, Nk, d);
   if (st != FA_OK) return st;
   const void* all[] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : all)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  const size_t need = fa_bwd_workspace_size(B, H, Nq, d);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * N * H * d * 2, lb = (size_t)B * H * N * 4;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * H * d * 2, lb = (size_t)B * H * Nq * 4;
   const void* ins[6] = {q, k, v, o, dO, lse};
-  const size_t insz[6] = {tb, tb, tb, tb, tb, lb};
+  const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
   void* outs[4] = {dq, dk, dv, workspace};
-  const size_t outsz[4] = {tb, tb, tb, need};
+  const size_t outsz[4] = {qb, kb, kb, need};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
@@ -138,11 +143,20 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   a.drow = static_cast<float*>(workspace);
   a.B = B;
   a.H = H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_bwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_qk(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, N, d, scale, causal, workspace, workspace_bytes,
+                   stream);
 }
 
 }  // extern "C"

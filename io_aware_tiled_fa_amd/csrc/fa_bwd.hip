@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const int t = threadIdx.x;
   const long row = (long)blockIdx.x * RPB + t / LPR;  // index over (b, n, h)
   const int sub = t % LPR;
-  const long nrows = (long)a.B * a.N * a.H;
+  const long nrows = (long)a.B * a.Nq * a.H;
   float acc = 0.f;
   if (row < nrows) {
     const size_t off = (size_t)row * D + 8 * sub;
@@ -75,11 +75,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   if (row < nrows && sub == 0) {
     const int h = (int)(row % a.H);
     const long bn = row / a.H;
-    const int n = (int)(bn % a.N);
-    const int b = (int)(bn / a.N);
-    const size_t r = ((size_t)b * a.H + h) * a.N + n;
+    const int n = (int)(bn % a.Nq);
+    const int b = (int)(bn / a.Nq);
+    const size_t r = ((size_t)b * a.H + h) * a.Nq + n;
     a.drow[r] = -acc;
-    a.drow[(size_t)a.B * a.H * a.N + r] = -a.lse[r] * kLog2e;
+    a.drow[(size_t)a.B * a.H * a.Nq + r] = -a.lse[r] * kLog2e;
   }
 }
 
@@ -165,15 +165,19 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   const int kg = w & 3;
   const int kb = kblk * BC;
   const int kw = kb + 32 * kg;  // first key of this wave's group
-  // N is a multiple of 64, so the last key block may hold only 64 keys:
-  // key groups past the end compute nothing
-  const bool group_active = kw < a.N;
+  // key groups past the last key compute nothing; the last active one may
+  // be ragged (its lanes past N_k are masked and store nothing)
+  const bool group_active = kw < a.Nk;
+  // causal: key j is visible to query i iff j <= i + off (keys aligned to the
+  // end of the query block)
+  const int off = a.Nk - a.Nq;
 
   const size_t rs = (size_t)a.H * D;
-  const size_t head_off = (size_t)b * a.N * rs + (size_t)h * D;
-  const size_t rowterm_off = ((size_t)b * a.H + h) * a.N;
+  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;   // Q, dO
+  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;  // K, V, dK, dV
+  const size_t rowterm_off = ((size_t)b * a.H + h) * a.Nq;
   const float* ndrow = a.drow + rowterm_off;
-  const float* nlse2 = a.drow + (size_t)a.B * a.H * a.N + rowterm_off;
+  const float* nlse2 = a.drow + (size_t)a.B * a.H * a.Nq + rowterm_off;
 
   // ---- per-lane LDS offsets.  Q / dO tiles use the forward kernel's
   // geometry; the swizzle XORs the chunk index, so a power-of-two chunk step
@@ -211,9 +215,10 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   }
   // rows 0 .. N - 1 at a stride of H d, the last ending H d - h d elements
   // before the end of the head's span; under 2^32 bytes since B N H d < 2^31
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
-  const buf_rsrc qrs = make_rsrc(a.q + head_off, head_bytes);
-  const buf_rsrc grs = make_rsrc(a.dO + head_off, head_bytes);
+  // (rows past N_q read zero)
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nq * a.H - h) * D * 2);
+  const buf_rsrc qrs = make_rsrc(a.q + q_off, head_bytes);
+  const buf_rsrc grs = make_rsrc(a.dO + q_off, head_bytes);
   // buffer I (a std::integral_constant) of each kind
   auto QT = [&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value & 3;
@@ -246,7 +251,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     // to the P^T / dS^T tiles never wait behind a copy the compiler cannot
     // tell apart from them
     if (w == 4) {  // lanes 0-31: -L log2 e, lanes 32-63: -D of the block's rows
-      const float* src = (l < 32) ? (nlse2 + qblk * BR + l) : (ndrow + qblk * BR + (l - 32));
+      // (rows past N_q repeat the last row; they are masked)
+      const int row = min(qblk * BR + (l & 31), a.Nq - 1);
+      const float* src = (l < 32) ? (nlse2 + row) : (ndrow + row);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)RT(I), 4, 0, 0);
     }
   };
@@ -256,16 +263,18 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   };
 
   const float c = a.c;
-  const int nqb = a.N / BR;
-  const int qstart = CAUSAL ? (kb / BR) : 0;
+  const int nqb = (a.Nq + BR - 1) / BR;
+  // causal: the first query block with a row that sees a key of this block
+  const int qstart = CAUSAL ? max(0, kb - off) / BR : 0;
   const int key = kw + l32;
-  const int nsteps = nqb - qstart + 1;
+  // no step when no query sees these keys (their gradients are then zero)
+  const int nsteps = qstart < nqb ? nqb - qstart + 1 : 0;
 
   // ---- the walk.  Step t produces P^T / dS^T of block qstart + t and
   // consumes block qstart + t - 1.  The two roles run separate loops (their
   // registers never live at the same time) with the same barriers: s_barrier
   // counts arrivals, so every wave passes one per step.
-  issue_q(qstart, IC<0>{});
+  if (qstart < nqb) issue_q(qstart, IC<0>{});
   if (qstart + 1 < nqb) issue_q(qstart + 1, IC<1>{});
   step_barrier();
 
@@ -274,9 +283,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     bf16x8 kreg[NKK], vreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) kreg[kk] = vreg[kk] = bf16x8{};
-    if (group_active) {
-      const __bf16* kr = a.k + head_off + (size_t)(kw + l32) * rs + 8 * h2;
-      const __bf16* vr = a.v + head_off + (size_t)(kw + l32) * rs + 8 * h2;
+    if (group_active && key < a.Nk) {
+      const __bf16* kr = a.k + kv_off + (size_t)key * rs + 8 * h2;
+      const __bf16* vr = a.v + kv_off + (size_t)key * rs + 8 * h2;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         kreg[kk] = *(const bf16x8*)(kr + 16 * kk);
@@ -351,11 +360,15 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) nlv[4 * g4 + i] = nl[i];
       }
+      // masked: key > query + off (causal), query >= N_q or key >= N_k
       const int q0 = qi * BR;
-      if (CAUSAL && q0 < kw + 31) {
+      if ((CAUSAL && q0 + off < kw + 31) || q0 + BR > a.Nq || kw + 32 > a.Nk) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          nlv[e] = (key > q0 + 8 * (e >> 2) + 4 * h2 + (e & 3)) ? -__builtin_inff() : nlv[e];
+        for (int e = 0; e < 16; ++e) {
+          const int qr = q0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          const bool masked = (CAUSAL && key > qr + off) || qr >= a.Nq || key >= a.Nk;
+          nlv[e] = masked ? -__builtin_inff() : nlv[e];
+        }
       }
       // block qi + 1's products beside block qi's softmax (the products of
       // the block past the end read a stale buffer and are never used)
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   auto consume = [&](int qi, const lds_char* __restrict__ qt, const lds_char* __restrict__ gt,
                      const lds_char* __restrict__ pt, const lds_char* __restrict__ dst)
       __attribute__((always_inline)) {
-    if (CAUSAL && qi * BR + BR - 1 < kw) return;  // P = dS = 0 for this block
+    if (CAUSAL && qi * BR + BR - 1 + off < kw) return;  // P = dS = 0 for this block
     typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
     // product i = (tq, db): A = P^T / dS^T chunks of the 16 queries of step
     // tq (queries 16 tq + 4 h2 + 0..3 and + 8), B = dO / Q columns by
@@ -444,9 +457,10 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kr = kw + 8 * (e >> 2) + 4 * h2 + (e & 3);
-      const size_t off = head_off + (size_t)kr * rs + 32 * db + l32;
-      a.dk[off] = (__bf16)(dkacc[db][e] * scale);
-      a.dv[off] = (__bf16)(dvacc[db][e]);
+      if (kr >= a.Nk) continue;
+      const size_t o = kv_off + (size_t)kr * rs + 32 * db + l32;
+      a.dk[o] = (__bf16)(dkacc[db][e] * scale);
+      a.dv[o] = (__bf16)(dvacc[db][e]);
     }
 }
 
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
   // ---- workgroup -> (batch, head, query tile), as in the forward kernel
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.Nq + BR - 1) / BR;
   const int nbh = a.B * a.H;
   const int wg = blockIdx.x;
   int bh, qi;
@@ -497,28 +511,32 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const int l = threadIdx.x & 63, h2 = l >> 5, l32 = l & 31;
   const int q0 = qb * BR;
   const int qw = q0 + 32 * w;
-  const bool wave_active = qw < a.N;
+  const bool wave_active = qw < a.Nq;
   const int qrow = qw + l32;
+  const bool row_valid = qrow < a.Nq;  // the last tile of rows may be ragged
+  // causal: key j is visible to query i iff j <= i + off
+  const int off = a.Nk - a.Nq;
 
   const size_t rs = (size_t)a.H * D;
-  const size_t head_off = (size_t)b * a.N * rs + (size_t)h * D;
-  const __bf16* kbase = a.k + head_off;
-  const __bf16* vbase = a.v + head_off;
+  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;   // Q, dO, dQ
+  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;  // K, V
+  const __bf16* kbase = a.k + kv_off;
+  const __bf16* vbase = a.v + kv_off;
 
   // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..), row terms
   bf16x8 qop[NKK], gop[NKK];
   float nl = 0.f, ndr = 0.f;  // -L log2(e) and -D of this lane's row
-  if (wave_active) {
-    const __bf16* qr = a.q + head_off + (size_t)qrow * rs + 8 * h2;
-    const __bf16* gr = a.dO + head_off + (size_t)qrow * rs + 8 * h2;
+  if (row_valid) {
+    const __bf16* qr = a.q + q_off + (size_t)qrow * rs + 8 * h2;
+    const __bf16* gr = a.dO + q_off + (size_t)qrow * rs + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       qop[kk] = *(const bf16x8*)(qr + 16 * kk);
       gop[kk] = *(const bf16x8*)(gr + 16 * kk);
     }
-    const size_t r = ((size_t)b * a.H + h) * a.N + qrow;
+    const size_t r = ((size_t)b * a.H + h) * a.Nq + qrow;
     ndr = a.drow[r];
-    nl = a.drow[(size_t)a.B * a.H * a.N + r];
+    nl = a.drow[(size_t)a.B * a.H * a.Nq + r];
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qop[kk] = gop[kk] = bf16x8{};
@@ -547,7 +565,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     const int row = p / NCH, ch = p % NCH;
     goff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.H - h) * D * 2);  // (rows past N_k read zero)
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
   const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
@@ -560,9 +578,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  const int ntiles_all = a.N / BC;
+  const int ntiles_all = (a.Nk + BC - 1) / BC;
   int ntiles = ntiles_all;
-  if (CAUSAL) ntiles = min(ntiles_all, (min(q0 + BR, a.N) - 1) / BC + 1);
+  if (CAUSAL) {
+    const int last_key = min(q0 + BR, a.Nq) - 1 + off;  // last key any row here sees
+    ntiles = last_key < 0 ? 0 : min(ntiles_all, last_key / BC + 1);
+  }
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -572,6 +593,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   auto compute_tile = [&](auto MASK, int kb, const lds_char* __restrict__ kt_lds,
                           const lds_char* __restrict__ vt_lds) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
+    const int lim = CAUSAL ? min(qrow + off, a.Nk - 1) : a.Nk - 1;  // last visible key
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       // S^T and dP^T of the 32-key sub-block: lane holds [key 8(e/4)+4h2+e%4][query l32];
@@ -600,10 +622,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int e = 0; e < 16; e += 2) {
         float p0 = fast_exp2(fmaf(sacc[e], c, nl));
         float p1 = fast_exp2(fmaf(sacc[e + 1], c, nl));
-        if constexpr (MASKED) {
+        if constexpr (MASKED) {  // key > query + off (causal) or key >= N_k
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          p0 = (key > qrow) ? 0.f : p0;
-          p1 = (key + 1 > qrow) ? 0.f : p1;
+          p0 = (key > lim) ? 0.f : p0;
+          p1 = (key + 1 > lim) ? 0.f : p1;
         }
         dspk[e >> 1] = pack_bf16x2(p0 * (pacc[e] + ndr), p1 * (pacc[e + 1] + ndr));
       }
@@ -626,34 +648,50 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  auto tile_step = [&](int kt, const lds_char* __restrict__ kt_lds, const lds_char* __restrict__ vt_lds,
-                       lds_char* __restrict__ knext, lds_char* __restrict__ vnext) __attribute__((always_inline)) {
+  // MAYMASK: whether the tile can need masking (causal diagonal tiles, or
+  // the ragged last tile); non-causal loops never instantiate the masked
+  // variant and take their ragged last tile after the loop
+  auto tile_step = [&](auto MAYMASK, int kt, const lds_char* __restrict__ kt_lds,
+                       const lds_char* __restrict__ vt_lds, lds_char* __restrict__ knext,
+                       lds_char* __restrict__ vnext) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
     if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
     const int kb = kt * BC;
     if (!wave_active) return;
-    if (CAUSAL && kb > qw + 31) return;  // whole tile in this wave's future
-    if (CAUSAL && kb + BC - 1 > qw)
-      compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
-    else
+    if (CAUSAL && kb > qw + 31 + off) return;  // whole tile in this wave's future
+    if constexpr (decltype(MAYMASK)::value) {
+      if ((CAUSAL && kb + BC - 1 > qw + off) || kb + BC > a.Nk)
+        compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
+      else
+        compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
+    } else {
       compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
+    }
   };
 
   lds_char* K0 = (lds_char*)k_lds0;
   lds_char* K1 = (lds_char*)k_lds1;
   lds_char* V0 = (lds_char*)v_lds0;
   lds_char* V1 = (lds_char*)v_lds1;
-  issue_tile(0, K0, V0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_step(kt, K0, V0, K1, V1);
-    if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
+  constexpr auto LOOP_MASK = std::integral_constant<bool, CAUSAL>{};
+  const int nloop = (!CAUSAL && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
+  if (ntiles > 0) issue_tile(0, K0, V0);
+  for (int kt = 0; kt < nloop; kt += 2) {
+    tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
+    if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
+  }
+  if (nloop < ntiles) {  // the ragged last tile of a non-causal walk
+    if (nloop & 1)
+      tile_step(std::true_type{}, nloop, K1, V1, K0, V0);
+    else
+      tile_step(std::true_type{}, nloop, K0, V0, K1, V1);
   }
 
-  if (!wave_active) return;
+  if (!row_valid) return;
   // ---- dQ = scale dQ^T; lane holds [d = 32 db + 8(e/4)+4h2+e%4][query l32]
   const float scale = a.scale;
-  __bf16* dqrow = a.dq + head_off + (size_t)qrow * rs;
+  __bf16* dqrow = a.dq + q_off + (size_t)qrow * rs;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -669,21 +707,21 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   void* args[] = {(void*)&a};
   {
-    const long rows = (long)a.B * a.N * a.H;
+    const long rows = (long)a.B * a.Nq * a.H;
     const int rpb = 256 / (D / 8);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     hipError_t e = hipLaunchKernel((const void*)bwd_pre_kernel<D>, grid, dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
-    dim3 grid((unsigned)(a.B * a.H * ((a.N + 127) / 128)));
+    dim3 grid((unsigned)(a.B * a.H * ((a.Nk + 127) / 128)));
     hipError_t e = hipLaunchKernel((const void*)bwd_main_kernel<D, CAUSAL>, grid, dim3(512), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
     constexpr int NW = D == 128 ? 8 : 4;
     constexpr int BR = NW * 32;
-    dim3 grid((unsigned)(a.B * a.H * ((a.N + BR - 1) / BR)));
+    dim3 grid((unsigned)(a.B * a.H * ((a.Nq + BR - 1) / BR)));
     return hipLaunchKernel((const void*)bwd_dq_kernel<D, NW, 64, CAUSAL>, grid, dim3(NW * 64), args, 0, stream);
   }
 }

@@ -38,14 +38,11 @@
 
 namespace fa {
 
-// LT keys are copied per barrier, computed as LT / BC tiles of BC keys.
-template <int D, int NW, int BC, int LT, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
-  constexpr int TILEB = LT * ROWB;       // bytes of one K or V load tile
-  constexpr int SUB = LT / BC;           // compute tiles per load tile
-  static_assert(SUB * BC == LT, "load tile must hold whole compute tiles");
+  constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
   constexpr int NCH = D / 8;             // 16-byte chunks per row
   constexpr int LOADS = TILEB / 1024;    // 1 KiB wave copies per tile
   constexpr int LPW = LOADS / NW;        // copies per wave per tile
@@ -65,7 +62,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
   // ---- workgroup -> (batch, head, query tile)
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.Nq + BR - 1) / BR;
   const int nbh = a.B * a.H;
   const int wg = blockIdx.x;
   int bh, qi;
@@ -87,19 +84,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const int l32 = l & 31;  // query row of this lane within the wave's 32
   const int q0 = qb * BR;
   const int qw = q0 + 32 * w;
-  const bool wave_active = qw < a.N;
+  const bool wave_active = qw < a.Nq;
+  const int qrow = qw + l32;
+  const bool row_valid = qrow < a.Nq;  // the last tile of rows may be ragged
+  // causal: key j is visible to query i iff j <= i + off (keys aligned to the
+  // end of the query block); rows with i + off < 0 see no key
+  const int off = a.Nk - a.Nq;
 
   const size_t rs = (size_t)a.H * D;  // elements between consecutive rows
-  const size_t head_off = (size_t)b * a.N * rs + (size_t)h * D;
-  const __bf16* kbase = a.k + head_off;
-  const __bf16* vbase = a.v + head_off;
+  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;
+  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;
+  const __bf16* kbase = a.k + kv_off;
+  const __bf16* vbase = a.v + kv_off;
 
   // ---- Q tile -> B operand registers (lane: row l32, d = 16 kk + 8 h2 .. +7)
   bf16x8 qop[NKK];
-  if (wave_active) {
-    const __bf16* qrow = a.q + head_off + (size_t)(qw + l32) * rs + 8 * h2;
+  if (row_valid) {
+    const __bf16* qrow_p = a.q + q_off + (size_t)qrow * rs + 8 * h2;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qop[kk] = *(const bf16x8*)(qrow + 16 * kk);
+    for (int kk = 0; kk < NKK; ++kk) qop[kk] = *(const bf16x8*)(qrow_p + 16 * kk);
     if (a.negate) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -151,11 +154,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // K and V of this (batch, head) as buffer resources: rows 0 .. N - 1 at a
   // stride of H d elements, the last ending H d - h d elements before the
   // end of the head's span; under 2^32 bytes since B N H d < 2^31
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.N * a.H - h) * D * 2);
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.H - h) * D * 2);
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
   const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(LT * rs * 2);
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
@@ -165,11 +168,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
 
   // ---- key tiles this workgroup visits
-  const int ntiles_all = (a.N + LT - 1) / LT;
+  const int ntiles_all = (a.Nk + BC - 1) / BC;
   int ntiles = ntiles_all;
   if (CAUSAL) {
-    const int last_row = min(q0 + BR, a.N) - 1;
-    ntiles = min(ntiles_all, last_row / LT + 1);
+    const int last_key = min(q0 + BR, a.Nq) - 1 + off;  // last key any row here sees
+    ntiles = last_key < 0 ? 0 : min(ntiles_all, last_key / BC + 1);
   }
 
   f32x16 oacc[NDB];
@@ -178,12 +181,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -__builtin_inff();  // running max, base-2 scaled units
   float l_run = 0.f;                // this lane's half of the running sum
   const float c = a.c;
-  const int qrow = qw + l32;
 
   // Work on one key tile held in LDS.  MASK (std::true_type or
   // std::false_type) selects the variant for tiles crossing this wave's
   // diagonal; every other tile runs without a single masking instruction.
-  auto compute_tile = [&](auto MASK, int kb, const lds_char* kt_lds, const lds_char* vt_lds) {
+  auto compute_tile = [&](auto MASK, int kb, const lds_char* kt_lds, const lds_char* vt_lds) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
     // S^T (keys x queries) for each 32-key sub-block.  All K operands of a
     // sub-block are requested from LDS before its first product so the
@@ -203,12 +205,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     // scale factor c is never 0 (the host clamps it to a tiny positive
     // number), so exp2(-inf * c - m) below is exactly 0 with no second mask.
     if constexpr (MASKED) {
+      // key > qrow + off (causal) or key >= Nk (past the keys)
+      const int lim = CAUSAL ? min(qrow + off, a.Nk - 1) : a.Nk - 1;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          sacc[sb][e] = (key > qrow) ? -__builtin_inff() : sacc[sb][e];
+          sacc[sb][e] = (key > lim) ? -__builtin_inff() : sacc[sb][e];
         }
     }
 
@@ -232,8 +236,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       l_run *= alpha;
     }
 
-    // probabilities, rounded to bf16 pairs for the PV product
-    const float negm = -m_run;
+    // probabilities, rounded to bf16 pairs for the PV product (a row that has
+    // seen no key yet keeps m = -inf and every p = 0)
+    const float negm = (m_run == -__builtin_inff()) ? 0.f : -m_run;
     uint32_t pk[NSB][8];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
@@ -265,25 +270,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   };
 
   // one key tile: wait for its copies, start the next tile's copies into
-  // the other buffer, then compute on this one
-  auto tile_step = [&](int kt, const lds_char* kt_lds, const lds_char* vt_lds,
-                       lds_char* knext, lds_char* vnext) {
+  // the other buffer, then compute on this one.  MAYMASK (std::true_type /
+  // std::false_type) says whether the tile can need masking: causal tiles
+  // crossing a wave's diagonal, or the ragged last tile (keys past N_k, which
+  // the copy read as zeros).  Non-causal loops never instantiate the masked
+  // variant; their ragged last tile is peeled off the loop.
+  auto tile_step = [&](auto MAYMASK, int kt, const lds_char* kt_lds, const lds_char* vt_lds,
+                       lds_char* knext, lds_char* vnext) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
     if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
     if (!wave_active) return;
-#pragma unroll
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int kb = kt * LT + sub * BC;
-      // past the keys (the load tile's copy read zeros there), or whole
-      // tile in this wave's future
-      if (kb >= a.N || (CAUSAL && kb > qw + 31)) return;
-      const lds_char* ks = kt_lds + sub * BC * ROWB;
-      const lds_char* vs = vt_lds + sub * BC * ROWB;
-      if (CAUSAL && kb + BC - 1 > qw)
-        compute_tile(std::true_type{}, kb, ks, vs);
+    const int kb = kt * BC;
+    if (CAUSAL && kb > qw + 31 + off) return;  // whole tile in this wave's future
+    if constexpr (decltype(MAYMASK)::value) {
+      if ((CAUSAL && kb + BC - 1 > qw + off) || kb + BC > a.Nk)
+        compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
       else
-        compute_tile(std::false_type{}, kb, ks, vs);
+        compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
+    } else {
+      compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
     }
   };
 
@@ -291,17 +297,27 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   lds_char* K1 = (lds_char*)k_lds1;
   lds_char* V0 = (lds_char*)v_lds0;
   lds_char* V1 = (lds_char*)v_lds1;
-  issue_tile(0, K0, V0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_step(kt, K0, V0, K1, V1);
-    if (kt + 1 < ntiles) tile_step(kt + 1, K1, V1, K0, V0);
+  constexpr auto LOOP_MASK = std::integral_constant<bool, CAUSAL>{};
+  const int nloop = (!CAUSAL && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
+  if (ntiles > 0) issue_tile(0, K0, V0);
+  for (int kt = 0; kt < nloop; kt += 2) {
+    tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
+    if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
+  }
+  if (nloop < ntiles) {  // the ragged last tile of a non-causal walk
+    if (nloop & 1)
+      tile_step(std::true_type{}, nloop, K1, V1, K0, V0);
+    else
+      tile_step(std::true_type{}, nloop, K0, V0, K1, V1);
   }
 
   if (!wave_active) return;
-  // ---- epilogue: O = O_acc / l in bf16, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = O_acc / l in bf16, LSE = (m + log2 l) ln 2; a row
+  // that saw no key gets O = 0 and LSE = -inf
   const float lt = sum_cross_half(l_run);
-  const float inv = fast_rcp(lt);
-  __bf16* orow = a.o + head_off + (size_t)qrow * rs;
+  const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
+  if (!row_valid) return;
+  __bf16* orow = a.o + q_off + (size_t)qrow * rs;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -311,31 +327,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
       *(u32x2*)(orow + d0) = val;
     }
-  if (h2 == 0) a.lse[((size_t)b * a.H + h) * a.N + qrow] = (m_run + fast_log2(lt)) * kLn2;
+  if (h2 == 0)
+    a.lse[((size_t)b * a.H + h) * a.Nq + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -__builtin_inff();
 }
 
-template <int D, int NW, int BC, int LT, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32;
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.Nq + BR - 1) / BR;
   dim3 grid((unsigned)(a.B * a.H * nqb));
   dim3 block(NW * 64);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, LT, CAUSAL>, grid, block, args, 0, stream);
+  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, CAUSAL>, grid, block, args, 0, stream);
 }
-
-// keys copied per barrier (64: measured faster than 128 or 256 at both d)
-#ifndef FWD_LT128
-#define FWD_LT128 64
-#endif
-#ifndef FWD_LT64
-#define FWD_LT64 64
-#endif
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_fwd_t<128, 8, 64, FWD_LT128, true>(a, stream) : launch_fwd_t<128, 8, 64, FWD_LT128, false>(a, stream);
-  return causal ? launch_fwd_t<64, 4, 64, FWD_LT64, true>(a, stream) : launch_fwd_t<64, 4, 64, FWD_LT64, false>(a, stream);
+    return causal ? launch_fwd_t<128, 8, 64, true>(a, stream) : launch_fwd_t<128, 8, 64, false>(a, stream);
+  return causal ? launch_fwd_t<64, 4, 64, true>(a, stream) : launch_fwd_t<64, 4, 64, false>(a, stream);
 }
 
 }  // namespace fa

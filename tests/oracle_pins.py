@@ -216,14 +216,82 @@ def pin_brute_force_forward(orc):
 def pin_brute_force_backward(orc):
     """Pure-Python chain rule agrees with the oracle's gradients to 1e-12."""
     rng = np.random.default_rng(32)
-    for (n, d, causal) in ((7, 4, False), (10, 6, True), (16, 8, True)):
-        q, k, v, do = (_rand(rng, 1, n, 1, d) for _ in range(4))
+    for (n_q, n_k, d, causal) in ((7, 7, 4, False), (10, 10, 6, True), (16, 16, 8, True),
+                                  (5, 9, 4, False), (6, 11, 5, True), (11, 6, 3, True)):
+        q, do = _rand(rng, 1, n_q, 1, d), _rand(rng, 1, n_q, 1, d)
+        k, v = _rand(rng, 1, n_k, 1, d), _rand(rng, 1, n_k, 1, d)
         dq, dk, dv = orc.attention_backward(q, k, v, do, 0.7, causal)
         bq, bk, bv = brute_backward(q[0, :, 0].tolist(), k[0, :, 0].tolist(),
                                     v[0, :, 0].tolist(), do[0, :, 0].tolist(), 0.7, causal)
         _close(dq[0, :, 0], np.array(bq), 1e-12, "brute dQ")
         _close(dk[0, :, 0], np.array(bk), 1e-12, "brute dK")
         _close(dv[0, :, 0], np.array(bv), 1e-12, "brute dV")
+
+
+def pin_torch_float64_cross(orc):
+    """N_q != N_k: torch CPU float64 attention with an explicit mask that aligns
+    the keys to the end of the query block agrees to 1e-12, gradients too.
+    (Only shapes where every query sees a key: torch returns NaN otherwise.)"""
+    import torch
+
+    rng = np.random.default_rng(34)
+    for (n_q, n_k, causal) in ((19, 41, True), (19, 41, False), (41, 19, False)):
+        B, H, d = 1, 2, 8
+        q, do = _rand(rng, B, n_q, H, d), _rand(rng, B, n_q, H, d)
+        k, v = _rand(rng, B, n_k, H, d), _rand(rng, B, n_k, H, d)
+        tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), dtype=torch.float64,
+                                   requires_grad=True) for x in (q, k, v))
+        i = torch.arange(n_q)[:, None]
+        j = torch.arange(n_k)[None, :]
+        mask = (j <= i + (n_k - n_q)) if causal else torch.ones(n_q, n_k, dtype=torch.bool)
+        to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.6)
+        to.backward(torch.tensor(do.transpose(0, 2, 1, 3), dtype=torch.float64))
+        o, lse = orc.attention_forward(q, k, v, 0.6, causal)
+        _close(o, to.detach().numpy().transpose(0, 2, 1, 3), 1e-12, f"torch O {n_q}x{n_k}")
+        s_ = (0.6 * torch.matmul(tq.detach(), tk.detach().transpose(-1, -2))).masked_fill(~mask, -float("inf"))
+        _close(lse, torch.logsumexp(s_, dim=-1).numpy(), 1e-12, f"torch LSE {n_q}x{n_k}")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.6, causal)
+        for name, mine, ref in (("dQ", dq, tq.grad), ("dK", dk, tk.grad), ("dV", dv, tv.grad)):
+            _close(mine, ref.numpy().transpose(0, 2, 1, 3), 1e-12, f"torch {name} {n_q}x{n_k}")
+
+
+def pin_suffix_queries(orc):
+    """Causal with N_q < N_k is the last N_q rows of square causal attention
+    over all N_k positions; the gradients are those of the square problem with
+    dO = 0 on its first N_k - N_q rows.  With N_q > N_k the first N_q - N_k
+    rows see no key: O = 0, LSE = -inf, dQ = 0, and they add nothing to dK, dV."""
+    rng = np.random.default_rng(35)
+    n_q, n_k, H, d = 6, 15, 2, 5
+    qq, kk, vv = (_rand(rng, 1, n_k, H, d) for _ in range(3))
+    do = _rand(rng, 1, n_q, H, d)
+    o_full, lse_full = orc.attention_forward(qq, kk, vv, 0.45, True)
+    o, lse = orc.attention_forward(qq[:, n_k - n_q:], kk, vv, 0.45, True)
+    _close(o, o_full[:, n_k - n_q:], 1e-13, "suffix O")
+    _close(lse, lse_full[:, :, n_k - n_q:], 1e-13, "suffix LSE")
+    do_full = np.zeros((1, n_k, H, d))
+    do_full[:, n_k - n_q:] = do
+    gq_full, gk_full, gv_full = orc.attention_backward(qq, kk, vv, do_full, 0.45, True)
+    gq, gk, gv = orc.attention_backward(qq[:, n_k - n_q:], kk, vv, do, 0.45, True)
+    _close(gq, gq_full[:, n_k - n_q:], 1e-13, "suffix dQ")
+    _close(gk, gk_full, 1e-13, "suffix dK")
+    _close(gv, gv_full, 1e-13, "suffix dV")
+
+    # N_q > N_k: the rows past the first N_q - N_k are the square problem
+    n_q, n_k = 13, 4
+    q, do = _rand(rng, 1, n_q, H, d), _rand(rng, 1, n_q, H, d)
+    k, v = _rand(rng, 1, n_k, H, d), _rand(rng, 1, n_k, H, d)
+    o, lse = orc.attention_forward(q, k, v, 0.45, True)
+    gq, gk, gv = orc.attention_backward(q, k, v, do, 0.45, True)
+    e = n_q - n_k
+    assert np.all(o[:, :e] == 0.0) and np.all(np.isneginf(lse[:, :, :e])), "empty rows: O = 0, LSE = -inf"
+    assert np.all(gq[:, :e] == 0.0), "empty rows: dQ = 0"
+    o_sq, lse_sq = orc.attention_forward(q[:, e:], k, v, 0.45, True)
+    _close(o[:, e:], o_sq, 1e-13, "tail O")
+    _close(lse[:, :, e:], lse_sq, 1e-13, "tail LSE")
+    sq_q, sq_k, sq_v = orc.attention_backward(q[:, e:], k, v, do[:, e:], 0.45, True)
+    _close(gq[:, e:], sq_q, 1e-13, "tail dQ")
+    _close(gk, sq_k, 1e-13, "tail dK")
+    _close(gv, sq_v, 1e-13, "tail dV")
 
 
 def pin_torch_float64(orc):
@@ -258,8 +326,10 @@ def pin_finite_differences(orc):
     """Central differences of L = sum(O * dO) match the gradients (rel 1e-6)."""
     rng = np.random.default_rng(41)
     eps = 1e-6
-    for (n, d, causal) in ((5, 3, False), (6, 4, True), (8, 4, True)):
-        q, k, v, do = (_rand(rng, 1, n, 1, d) for _ in range(4))
+    for (n_q, n_k, d, causal) in ((5, 5, 3, False), (6, 6, 4, True), (8, 8, 4, True),
+                                  (4, 7, 3, True), (7, 4, 3, True), (3, 6, 2, False)):
+        q, do = _rand(rng, 1, n_q, 1, d), _rand(rng, 1, n_q, 1, d)
+        k, v = _rand(rng, 1, n_k, 1, d), _rand(rng, 1, n_k, 1, d)
         scale = 0.9
         grads = orc.attention_backward(q, k, v, do, scale, causal)
 
@@ -316,6 +386,8 @@ ALL_PINS = [
     pin_brute_force_forward,
     pin_brute_force_backward,
     pin_torch_float64,
+    pin_torch_float64_cross,
+    pin_suffix_queries,
     pin_finite_differences,
     pin_gradient_identities,
 ]

@@ -112,18 +112,24 @@ U_BF16 = 2.0 ** -8
 
 
 def _probabilities(q, k, scale, causal):
+    """Softmax rows for the bounds; under the causal mask the keys are aligned
+    to the end of the queries, and a row that sees no key is all zero."""
     s = scale * (q @ k.T)
+    n_q, n_k = s.shape
     if causal:
-        s = np.where(np.tril(np.ones(s.shape, dtype=bool)), s, -np.inf)
+        vis = np.arange(n_k)[None, :] <= np.arange(n_q)[:, None] + (n_k - n_q)
+        s = np.where(vis, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
+    tot = e.sum(axis=1, keepdims=True)
+    return e / np.where(tot > 0, tot, 1.0)
 
 
 def forward_error_bound(q, k, v, scale, causal):
     """Per-element bound for O, layout [B, N, H, d]."""
     B, N, H, d = q.shape
-    out = np.empty((B, N, H, d))
+    out = np.empty((B, N, H, v.shape[3]))
     for b in range(B):
         for h in range(H):
             p = _probabilities(q[b, :, h].astype(np.float64), k[b, :, h].astype(np.float64), scale, causal)
@@ -134,7 +140,8 @@ def forward_error_bound(q, k, v, scale, causal):
 def backward_error_bound(q, k, v, do, o_ref, scale, causal):
     """Per-element bounds for (dQ, dK, dV), layouts like the inputs."""
     B, N, H, d = q.shape
-    bq, bk, bv = (np.empty((B, N, H, d)) for _ in range(3))
+    n_k = k.shape[1]
+    bq, bk, bv = np.empty((B, N, H, d)), np.empty((B, n_k, H, d)), np.empty((B, n_k, H, d))
     for b in range(B):
         for h in range(H):
             qh, kh, vh, gh = (x[b, :, h].astype(np.float64) for x in (q, k, v, do))

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
+        ["fa_fwd", "fa_fwd_qk", "fa_bwd", "fa_bwd_qk", "fa_bwd_workspace_size",
+         "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -64,8 +65,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, B=0, scale=float("nan")) == -2
     assert fwd(lib, H=-1, scale=float("nan")) == -2
     assert fwd(lib, B=2 ** 20, H=64, N=2 ** 16, d=128) == -2   # > 2^31 elements
-    assert fwd(lib, N=100, scale=float("nan")) == -4
-    assert fwd(lib, N=96, scale=float("nan")) == -4
+    # any sequence length is accepted: the shape passes, the scale is refused
+    assert fwd(lib, N=100, scale=float("nan")) == -7
+    assert fwd(lib, N=1, scale=float("nan")) == -7
     assert fwd(lib, q=P[0] + 8, scale=float("nan")) == -5
     assert fwd(lib, lse=P[4] + 4, scale=float("nan")) == -5
     assert fwd(lib, scale=float("nan")) == -7
@@ -90,7 +92,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, dv=None) == -1
     assert bwd(lib, d=32) == -3
     assert bwd(lib, N=0) == -2
-    assert bwd(lib, N=65) == -4
+    assert bwd(lib, N=65, scale=float("nan")) == -7   # ragged length passes the shape checks
     assert bwd(lib, dk=P[7] + 2) == -5
     assert bwd(lib, ws=None) == -6
     assert bwd(lib, ws_bytes=1023) == -6               # one byte short of the 1024 needed
@@ -100,6 +102,38 @@ def test_bwd_validation(lib):
     assert bwd(lib, dq=P[1]) == -9                    # dQ aliases K
     assert bwd(lib, dk=P[6]) == -9                    # dK aliases dQ
     assert bwd(lib, ws=P[8]) == -9                    # workspace aliases dV
+
+
+def fwd_qk(lib, Nq=128, Nk=128, B=1, H=1, d=64, scale=0.125, causal=1, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4])
+    p.update(ptrs)
+    return lib.fa_fwd_qk(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, Nq, Nk, d, scale, causal, None)
+
+
+def bwd_qk(lib, Nq=128, Nk=128, B=1, H=1, d=64, scale=0.125, causal=1, ws=P[9], ws_bytes=None, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8])
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, Nq, d)
+    return lib.fa_bwd_qk(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                         B, H, Nq, Nk, d, scale, causal, ws, ws_bytes, None)
+
+
+def test_cross_shape_validation(lib):
+    assert fwd_qk(lib, Nq=0) == -2
+    assert fwd_qk(lib, Nk=0) == -2
+    assert fwd_qk(lib, Nk=-5) == -2
+    assert fwd_qk(lib, Nq=1, Nk=2 ** 31 - 1, H=2, d=128) == -2   # K holds > 2^31 elements
+    assert fwd_qk(lib, Nq=77, Nk=300, scale=float("nan")) == -7
+    assert fwd_qk(lib, Nq=300, Nk=77, d=80) == -3
+    assert fwd_qk(lib, o=P[1]) == -9                               # output aliases K
+    assert bwd_qk(lib, Nq=0) == -2
+    assert bwd_qk(lib, Nk=0) == -2
+    assert bwd_qk(lib, Nq=33, Nk=1000, scale=float("nan")) == -7
+    # the workspace is sized by the query length: one sized for N_k < N_q is refused
+    big = lib.fa_bwd_workspace_size(1, 1, 512, 64)
+    assert bwd_qk(lib, Nq=512, Nk=64, ws_bytes=lib.fa_bwd_workspace_size(1, 1, 64, 64)) == -6
+    assert bwd_qk(lib, Nq=512, Nk=64, ws_bytes=big, scale=float("nan")) == -7
 
 
 def test_workspace_size(lib):

@@ -1,0 +1,154 @@
+"""Any sequence length and cross attention (N_q != N_k): fa_fwd_qk and
+fa_bwd_qk through the C ABI against the fp64 oracle.
+
+Lengths are chosen to end ragged in every tile size the kernels use (query
+blocks of 128 or 256 rows in the forward, 32-row query blocks and 128-key
+blocks in the backward, 64-key tiles everywhere), including single rows and
+keys.  Under the causal mask the keys are aligned to the end of the query
+block (key j is visible to query i iff j <= i + N_k - N_q), so with
+N_q > N_k the first N_q - N_k rows see no key: their O and dQ must be exactly
+zero and their LSE -inf.
+
+O and LSE are held to the fixed gates.  The gradients are held, element by
+element, to the larger of the fixed gate and the error bound derived from the
+bfloat16 arithmetic (parity.py): with few keys each probability is large (1/5
+with five keys), so the bf16 rounding of dS enters every one of the N_q terms
+of a dK sum with a weight the long-sequence workloads never see.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_tiled_fa_amd.inputs import make_inputs
+from parity import (TOL_GRAD, TOL_LSE, TOL_O, TOL_O_MEAN, announce, backward_error_bound, compare,
+                    to_device, to_numpy_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from io_aware_tiled_fa_amd import binding
+
+    binding.load_library()
+    return binding
+
+
+def empty_rows(n_q, n_k, causal):
+    return max(0, n_q - n_k) if causal else 0
+
+
+def check_forward(fa, inp, causal, scale):
+    import torch
+
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_np, lse_np = to_numpy_f32(o), lse.cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal)
+    e = empty_rows(inp.N, inp.N_k, causal)
+    assert np.all(o_np[:, :e] == 0.0), "rows without a visible key must give O = 0"
+    assert np.all(np.isneginf(lse_np[:, :, :e])), "rows without a visible key must give LSE = -inf"
+    compare("O", o_np[:, e:], o_ref[:, e:], TOL_O, TOL_O_MEAN)
+    compare("LSE", lse_np[:, :, e:], lse_ref[:, :, e:], TOL_LSE, ulp_aware=False)
+    return q, k, v, o, lse
+
+
+def check_backward(fa, inp, causal, scale):
+    import torch
+
+    q, k, v, o, lse = check_forward(fa, inp, causal, scale)
+    do = to_device(inp.do_bits)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    o_ref, _ = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal)
+    bounds = backward_error_bound(inp.q, inp.k, inp.v, inp.do, o_ref, scale, causal)
+    e = empty_rows(inp.N, inp.N_k, causal)
+    dq_np = to_numpy_f32(dq)
+    assert np.all(dq_np[:, :e] == 0.0), "rows without a visible key must give dQ = 0"
+    for name, got, ref, bound in (("dQ", dq_np, rq, bounds[0]), ("dK", to_numpy_f32(dk), rk, bounds[1]),
+                                  ("dV", to_numpy_f32(dv), rv, bounds[2])):
+        compare(name, got, ref, TOL_GRAD, bound=np.maximum(bound, TOL_GRAD))
+
+
+SELF = [
+    # B, H, N, d, causal  (square, lengths that are not multiples of any tile)
+    (1, 1, 1, 64, False),
+    (1, 2, 1, 128, True),
+    (2, 3, 37, 64, True),
+    (2, 3, 100, 64, False),
+    (1, 2, 129, 128, True),
+    (1, 2, 129, 128, False),
+    (2, 2, 333, 128, True),
+    (1, 3, 601, 64, True),
+    (1, 2, 1000, 128, False),
+]
+
+CROSS = [
+    # B, H, N_q, N_k, d, causal
+    (1, 2, 64, 512, 128, True),     # queries at the end of a longer context
+    (2, 2, 100, 777, 64, True),
+    (2, 2, 100, 777, 64, False),
+    (1, 3, 600, 161, 128, False),
+    (1, 3, 600, 161, 128, True),    # 439 rows see no key
+    (1, 2, 300, 5, 64, False),      # one partial key tile
+    (1, 2, 300, 5, 128, True),
+    (2, 4, 1, 3000, 128, True),     # one query row (decode shape)
+    (1, 2, 3, 1, 64, False),
+    (1, 2, 257, 1023, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SELF)
+def test_forward_any_length(fa, B, H, N, d, causal):
+    announce(f"fwd any-length B={B} H={H} N={N} d={d} causal={causal}")
+    inp = make_inputs(B, H, N, d, seed=3000 + N + d)
+    check_forward(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", CROSS)
+def test_forward_cross(fa, B, H, Nq, Nk, d, causal):
+    announce(f"fwd cross B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    inp = make_inputs(B, H, Nq, d, N_k=Nk, seed=4000 + Nq + Nk + d)
+    check_forward(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SELF)
+def test_backward_any_length(fa, B, H, N, d, causal):
+    announce(f"bwd any-length B={B} H={H} N={N} d={d} causal={causal}")
+    inp = make_inputs(B, H, N, d, seed=5000 + N + d, with_do=True)
+    check_backward(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", CROSS)
+def test_backward_cross(fa, B, H, Nq, Nk, d, causal):
+    announce(f"bwd cross B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    inp = make_inputs(B, H, Nq, d, N_k=Nk, seed=6000 + Nq + Nk + d, with_do=True)
+    check_backward(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
+def test_cross_equals_suffix_of_self(fa):
+    """Causal cross attention of the last N_q queries over N_k keys equals the
+    last N_q rows of causal self-attention over all N_k positions, bit for
+    bit: both walk the same key tiles with the same mask for those rows.
+    Only holds where both launches put the rows in the same tile positions,
+    so N_k - N_q is a multiple of the forward's query block."""
+    import torch
+
+    announce("fwd cross == suffix of self")
+    Nk, Nq, d = 1536, 512, 128
+    inp = make_inputs(1, 4, Nk, d, seed=77)
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o_full, lse_full = fa.forward(q, k, v, causal=True)
+    o_suf, lse_suf = fa.forward(q[:, Nk - Nq:].contiguous(), k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_suf.view(torch.int16), o_full[:, Nk - Nq:].view(torch.int16))
+    assert torch.equal(lse_suf, lse_full[:, :, Nk - Nq:])

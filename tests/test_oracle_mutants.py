@@ -21,6 +21,10 @@ MUTANTS = {
                                "return j < (rows[:, None] + (n_k - n_q))"),
     "causal mask transposed": ("return j <= (rows[:, None] + (n_k - n_q))",
                                "return j >= (rows[:, None] + (n_k - n_q))"),
+    "causal keys aligned to the start": ("return j <= (rows[:, None] + (n_k - n_q))",
+                                         "return j <= rows[:, None]"),
+    "causal offset sign reversed": ("return j <= (rows[:, None] + (n_k - n_q))",
+                                    "return j <= (rows[:, None] + (n_q - n_k))"),
     "softmax summed over the wrong axis": ("l = e.sum(axis=1)", "l = e.sum(axis=0)"),
     "max shift not undone in LSE": ("m + np.log(np.where(l > 0, l, 1.0))",
                                     "np.log(np.where(l > 0, l, 1.0))"),
