@@ -19,24 +19,35 @@
  *     a softmax scale defaulting to 1/sqrt(head_dim), a causal flag) is the
  *     one in the holysheep.ai review, "Implementing Flash Attention in Your
  *     Architecture", and its shape checks in "Common Errors and Fixes",
- *     Error 4.
+ *     Error 4;
+ *   - grouped-query attention (fewer key / value heads than query heads)
+ *     and sliding-window attention (each token sees only nearby tokens) are
+ *     named as techniques used together with it in "Flash Attention
+ *     Explained", section "Flash Attention vs. Related Techniques"; the _ex
+ *     entry points take both.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are caller-owned DEVICE memory.  bf16 tensors are contiguous
  *    [B, N, H, d] (BSHD) with element (b, n, h, c) at ((b*N + n)*H + h)*d + c,
- *    where N is N_q for Q, O, dO, dQ and N_k for K, V, dK, dV (N_q = N_k = N
- *    for the entry points without the _qk suffix).  The log-sum-exp is
- *    contiguous float32 [B, H, N_q].
+ *    where N is N_q and H the query heads for Q, O, dO, dQ, and N is N_k and
+ *    H is H_kv for K, V, dK, dV (N_q = N_k = N and H_kv = H for fa_fwd and
+ *    fa_bwd; H_kv = H for the _qk entry points).  Query head h reads key /
+ *    value head h / (H / H_kv).  The log-sum-exp is contiguous float32
+ *    [B, H, N_q].
  *  - Base pointers must be 16-byte aligned.  Outputs must not alias inputs.
- *  - d must be 64 or 128.  B, H, N_q, N_k >= 1 (any length: the kernels
- *    mask ragged tiles), and each tensor must have fewer than 2^31 elements.
+ *  - d must be 64 or 128.  B, H, H_kv, N_q, N_k >= 1 (any length: the
+ *    kernels mask ragged tiles), H a multiple of H_kv, and each tensor must
+ *    have fewer than 2^31 elements.
  *  - scale is any finite float (0 allowed; negative allowed).
  *  - causal: 0 = every key visible; 1 = key j visible to query i iff
  *    j <= i + (N_k - N_q), i.e. the keys are aligned to the end of the
  *    queries (for N_q = N_k: j <= i).  When N_q > N_k the first N_q - N_k
  *    query rows see no key: their output row is 0, their log-sum-exp is
  *    -inf, and their dQ row is 0.
+ *  - window (the _ex entry points; 0 = none): with W > 0 query i also sees
+ *    only keys j with |i + (N_k - N_q) - j| < W, i.e. with causal = 1 the W
+ *    keys ending at its own position (itself and the W - 1 before it).
  *  - stream is a hipStream_t (NULL = the legacy default stream).  Calls only
  *    enqueue work and return; results are valid once the stream is
  *    synchronised.  The library allocates no memory and keeps no state
@@ -57,14 +68,14 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
-  FA_ERR_SHAPE = -2,      /* B, H, N_q or N_k not positive, or size overflow */
+  FA_ERR_SHAPE = -2,      /* a size not positive, H % H_kv != 0, or overflow */
   FA_ERR_HEADDIM = -3,    /* d is not 64 or 128                              */
   FA_ERR_SEQLEN = -4,     /* reserved: every length >= 1 is accepted          */
   FA_ERR_ALIGN = -5,      /* a base pointer is not 16-byte aligned           */
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required         */
   FA_ERR_SCALE = -7,      /* scale is NaN or infinite                        */
   FA_ERR_LAUNCH = -8,     /* the HIP launch reported an error                */
-  FA_ERR_ARG = -9         /* causal not 0/1, or outputs alias inputs         */
+  FA_ERR_ARG = -9         /* causal not 0/1, window < 0, or outputs alias    */
 } fa_status;
 
 /*
@@ -93,9 +104,21 @@ fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
 
 /*
+ * Forward pass, general form: H query heads over H_kv key / value heads
+ * (grouped-query attention; H_kv = 1 is multi-query attention), N_q query
+ * and N_k key rows, and an optional sliding window of W = window keys (see
+ * the conventions above).  q, o: [B, N_q, H, d]; k, v: [B, N_k, H_kv, d];
+ * lse: [B, H, N_q].  fa_fwd_qk is fa_fwd_ex with H_kv = H, window = 0.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
+                    void* stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for this shape: two float32
  * [B, H, N] row terms, -D_i = -sum_c dO_ic * O_ic and -lse_i * log2(e),
- * rounded up to a multiple of 256 bytes.  For fa_bwd_qk pass N = N_q.
+ * rounded up to a multiple of 256 bytes.  For fa_bwd_qk and fa_bwd_ex pass
+ * N = N_q and H = the number of query heads.
  * Returns 0 for an invalid shape.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -131,6 +154,20 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
 fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass, general form (the arguments of fa_fwd_ex).  q, o, dO, dq:
+ * [B, N_q, H, d]; k, v, dk, dv: [B, N_k, H_kv, d]; lse: [B, H, N_q] from
+ * fa_fwd_ex with the same arguments; workspace of at least
+ * fa_bwd_workspace_size(B, H, N_q, d) bytes.  dk and dv of a key / value
+ * head sum the contributions of every query head that reads it.  Keys that
+ * no query sees get dK = dV = 0.  fa_bwd_qk is fa_bwd_ex with H_kv = H,
+ * window = 0.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */

@@ -26,8 +26,8 @@ FA_STATUS = {
     -4: "FA_ERR_SEQLEN", -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE",
     -7: "FA_ERR_SCALE", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_bwd", "fa_bwd_qk", "fa_bwd_workspace_size", "fa_status_string",
-            "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_bwd", "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size",
+            "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_qk.restype = i
     lib.fa_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_ex.restype = i
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -88,8 +92,9 @@ def validate_attention_inputs(q, k, v) -> None:
             raise ValueError(f"{name} must be contiguous")
     if not (q.shape[0] == k.shape[0] == v.shape[0]):
         raise ValueError(f"Batch size mismatch: Q={q.shape[0]}, K={k.shape[0]}, V={v.shape[0]}")
-    if not (q.shape[2] == k.shape[2] == v.shape[2]):
-        raise ValueError(f"Num heads mismatch: Q={q.shape[2]}, K={k.shape[2]}, V={v.shape[2]}")
+    if k.shape[2] != v.shape[2] or q.shape[2] % k.shape[2] != 0:
+        raise ValueError(f"Num heads mismatch: Q={q.shape[2]}, K={k.shape[2]}, V={v.shape[2]} "
+                         "(K and V need equal heads, and Q a multiple of them)")
     if k.shape[1] != v.shape[1]:
         raise ValueError(f"Key/Value sequence length mismatch: K={k.shape[1]}, V={v.shape[1]}")
     if not (q.shape[3] == k.shape[3] == v.shape[3]):
@@ -111,15 +116,17 @@ def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 
 
-def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
+def forward(q, k, v, causal: bool = False, scale: Optional[float] = None, window: int = 0,
             out=None, lse=None, stream=None) -> Tuple[object, object]:
-    """O, LSE = fa_fwd_qk(Q, K, V); Q bf16 [B, N_q, H, d], K and V bf16
-    [B, N_k, H, d] on the GPU (N_q = N_k is plain self-attention)."""
+    """O, LSE = fa_fwd_ex(Q, K, V); Q bf16 [B, N_q, H, d], K and V bf16
+    [B, N_k, H_kv, d] on the GPU (N_q = N_k and H_kv = H is plain
+    self-attention; H_kv < H is grouped-query attention).  window > 0 limits
+    each query to the keys within that distance of its position."""
     import torch
 
     validate_attention_inputs(q, k, v)
     B, Nq, H, d = q.shape
-    Nk = k.shape[1]
+    Nk, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = default_scale(d)
     if out is None:
@@ -127,9 +134,10 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     lib = load_library()
-    st = lib.fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                       B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream_ptr(q.device, stream))
-    _check(lib, "fa_fwd_qk", st)
+    st = lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(window),
+                       _stream_ptr(q.device, stream))
+    _check(lib, "fa_fwd_ex", st)
     return out, lse
 
 
@@ -137,9 +145,9 @@ def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, N, d))
 
 
-def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None, window: int = 0,
              dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV = fa_bwd_qk(...); O and LSE are the forward's outputs."""
+    """dQ, dK, dV = fa_bwd_ex(...); O and LSE are the forward's outputs."""
     import torch
 
     validate_attention_inputs(q, k, v)
@@ -147,7 +155,7 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
         if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like Q")
     B, N, H, d = q.shape
-    Nk = k.shape[1]
+    Nk, Hkv = k.shape[1], k.shape[2]
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("LSE must be a contiguous float32 [B, H, N_q] tensor")
     if scale is None:
@@ -159,10 +167,10 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     need = int(lib.fa_bwd_workspace_size(B, H, N, d))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = lib.fa_bwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    st = lib.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       B, H, N, Nk, d, float(scale), int(bool(causal)),
+                       B, H, Hkv, N, Nk, d, float(scale), int(bool(causal)), int(window),
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                        _stream_ptr(q.device, stream))
-    _check(lib, "fa_bwd_qk", st)
+    _check(lib, "fa_bwd_ex", st)
     return dq, dk, dv

@@ -6,7 +6,7 @@
 // [batch, seq_len, num_heads, head_dim] tensors with matching batch, heads
 // and head_dim, and equal K / V lengths, while the query length may differ);
 // here Q, O, dO share one shape and K, V another, so they reduce to positive
-// B, H, N_q, N_k and a supported d.  The same page
+// B, H, H_kv, N_q, N_k, H a multiple of H_kv, and a supported d.  The same page
 // ("Common Errors and Fixes", Error 1) notes that a launch fails when a
 // tile exceeds device limits; here unsupported sizes are refused before
 // anything is launched.
@@ -25,13 +25,26 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Sizes: B, H, N_q, N_k >= 1, d in {64, 128}, and every tensor under 2^31
-// elements (the kernels index in 32-bit element offsets within a tensor).
-fa_status check_shape(int B, int H, int Nq, int Nk, int d) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+// Sizes: B, H, H_kv, N_q, N_k >= 1, H a multiple of H_kv, d in {64, 128},
+// and every tensor under 2^31 elements (the kernels index in 32-bit element
+// offsets within a tensor).
+fa_status check_shape(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if ((long long)B * Nq * H * d > 0x7FFFFFFFLL || (long long)B * Nk * H * d > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
+  if ((long long)B * Nq * H * d > 0x7FFFFFFFLL || (long long)B * Nk * Hkv * d > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
   return FA_OK;
+}
+
+// The visible band of query i: keys i + off - wl .. i + off + wr, off =
+// N_k - N_q.  An unbounded side gets N_q + N_k + 64, past every key of every
+// row; with N_q, N_k < 2^26 (each tensor < 2^31 elements, d >= 64) no sum
+// of these overflows an int.  Returns whether the band has an upper edge.
+bool band_of(int Nq, int Nk, int causal, int window, int& wl, int& wr) {
+  const int big = Nq + Nk + 64;
+  const int w = window > 0 ? (window - 1 < big ? window - 1 : big) : big;
+  wl = w;
+  wr = causal ? 0 : w;
+  return causal || window > 0;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -44,29 +57,30 @@ const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H, N_q and N_k must be positive and every tensor must have fewer than 2^31 elements";
+    case FA_ERR_SHAPE: return "B, H, H_kv, N_q and N_k must be positive, H a multiple of H_kv, and every tensor must have fewer than 2^31 elements";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_SEQLEN: return "sequence length not supported";
     case FA_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_SCALE: return "scale must be a finite float";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "causal must be 0 or 1 and outputs must not overlap inputs";
+    case FA_ERR_ARG: return "causal must be 0 or 1, window must not be negative, and outputs must not overlap inputs";
   }
   return "unknown status";
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
-fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
-                    int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                    void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, Nq, Nk, d);
+  fa_status st = check_shape(B, H, Hkv, Nq, Nk, d);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * H * d * 2, lb = (size_t)B * H * Nq * 4;
+  if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_ARG;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * Hkv * d * 2, lb = (size_t)B * H * Nq * 4;
   const void* ins[3] = {q, k, v};
   const size_t insz[3] = {qb, kb, kb};
   for (int i = 0; i < 3; ++i)
@@ -81,44 +95,52 @@ fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float*
   a.lse = lse;
   a.B = B;
   a.H = H;
+  a.Hkv = Hkv;
+  a.G = H / Hkv;
   a.Nq = Nq;
   a.Nk = Nk;
+  const bool band = band_of(Nq, Nk, causal, window, a.wl, a.wr);
   // scores enter the kernel as s * c in base 2.  c is kept away from 0: a
   // masked score (-inf) times c must stay -inf, and with scale == 0 a c of
   // 1e-30 leaves every finite s * c within 1e-24 of 0, where exp2 rounds to
   // exactly 1 in float32, as for c = 0.
   a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);
   a.negate = scale < 0.f;
-  const hipError_t e = fa::launch_fwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
+  const hipError_t e = fa::launch_fwd(a, d, band, window > 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, 0, stream);
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream) {
-  return fa_fwd_qk(q, k, v, o, lse, B, H, N, N, d, scale, causal, stream);
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, N, N, d, scale, causal, 0, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
-  if (check_shape(B, H, N, 1, d) != FA_OK) return 0;
+  if (check_shape(B, H, 1, N, 1, d) != FA_OK) return 0;
   return round256(2 * (size_t)B * H * N * sizeof(float));
 }
 
-fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, Nq, Nk, d);
+  fa_status st = check_shape(B, H, Hkv, Nq, Nk, d);
   if (st != FA_OK) return st;
   const void* all[] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : all)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_ARG;
   const size_t need = fa_bwd_workspace_size(B, H, Nq, d);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FA_ERR_WORKSPACE;
-  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * H * d * 2, lb = (size_t)B * H * Nq * 4;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * Hkv * d * 2, lb = (size_t)B * H * Nq * 4;
   const void* ins[6] = {q, k, v, o, dO, lse};
   const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
   void* outs[4] = {dq, dk, dv, workspace};
@@ -143,20 +165,31 @@ fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
   a.drow = static_cast<float*>(workspace);
   a.B = B;
   a.H = H;
+  a.Hkv = Hkv;
+  a.G = H / Hkv;
   a.Nq = Nq;
   a.Nk = Nk;
+  const bool band = band_of(Nq, Nk, causal, window, a.wl, a.wr);
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
-  const hipError_t e = fa::launch_bwd(a, d, causal != 0, static_cast<hipStream_t>(stream));
+  const hipError_t e = fa::launch_bwd(a, d, band, window > 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, 0, workspace,
+                   workspace_bytes, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  int B, int H, int N, int d, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_bwd_qk(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, N, d, scale, causal, workspace, workspace_bytes,
-                   stream);
+  return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, H, N, N, d, scale, causal, 0, workspace,
+                   workspace_bytes, stream);
 }
 
 }  // extern "C"

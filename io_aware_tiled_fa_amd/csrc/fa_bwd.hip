@@ -11,26 +11,22 @@
 // P_ij = exp(s_ij - L_i), and the softmax Jacobian term sum_j P_ij dP_ij
 // equals D_i = sum_c dO_ic O_ic, so no row of P is ever needed whole.
 //
-// Three kernels on one stream:
-//  1. bwd_pre: D_i = dO_i . O_i and -L_i log2(e) per row (float32), and the
-//     float32 dQ accumulator cleared;
-//  2. bwd_main: one workgroup per 128-key block of one (batch, head); each
-//     of its 4 waves keeps 32 keys of K and V in registers and their dK, dV
-//     in float32 accumulators (AGPRs), and walks the query blocks (64 rows
-//     each, all of them, or those at or after the diagonal when causal)
-//     staged through LDS with double-buffered direct copies.  Per query
-//     block and wave:
-//        S  = Q K^T,  P = exp2(S scale log2e - L log2e)   (masked on the diagonal)
-//        dV += P^T dO
-//        dP = dO V^T, dS = P (dP - D)
-//        dK += dS^T Q
-//     then dS (bf16) goes to LDS and the waves split dQ_blk = dS K over the
-//     output columns and add it into the float32 accumulator atomically;
-//  3. bwd_dq: dQ = scale * accumulator, rounded to bf16.
-// All products run on v_mfma_f32_32x32x16_bf16 in the "S layout": lane l
-// holds 16 queries of key l % 32, which is directly the A operand of the
-// dV and dK products; the dO and Q tiles feed the B operand through
-// transpose reads, exactly as V does in the forward kernel.
+// Three kernels on one stream, none of them atomic, so the gradients are
+// the same bit for bit on every run:
+//  1. bwd_pre: -D_i = -dO_i . O_i and -L_i log2(e) per row (float32);
+//  2. bwd_main (dK, dV): one workgroup of 8 waves per 128-key block of one
+//     (batch, key head).  Four producer waves recompute S = Q K^T, P and
+//     dS = P (dP - D) for 32 keys each against 32-query blocks staged in
+//     LDS; the consumer wave on the same SIMD adds P^T dO and dS^T Q into
+//     dV and dK, one block behind.  The walk covers every query block of
+//     every query head that reads this key head (grouped-query attention)
+//     whose rows see a key of the block;
+//  3. bwd_dq (dQ): one workgroup per query tile, walking the key tiles like
+//     the forward kernel and recomputing S and dP; dQ is summed in
+//     registers and written once.
+// Masks: key j is visible to query i iff i + off - wl <= j <= i + off + wr
+// (off = N_k - N_q), the forward kernel's band.
+// All products run on v_mfma_f32_32x32x16_bf16.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -107,8 +103,9 @@ __device__ __forceinline__ int pt_off(int row, int q) {
   return row * 64 + (((q >> 2) ^ ((row >> 2) & 7)) << 3) + 2 * (q & 3);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND, bool WIN>
 __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
+  static_assert(BAND || !WIN, "a window always bounds the keys above");
   constexpr int BC = 128;              // keys per workgroup (4 groups of 32)
   constexpr int BR = 32;               // queries per step
   constexpr int ROWB = D * 2;          // bytes per row of a Q / dO tile
@@ -144,7 +141,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(256))) float r_lds2[2 * BR];
   __shared__ __attribute__((aligned(256))) float r_lds3[2 * BR];
 
-  const int nbh = a.B * a.H;
+  // one workgroup per (batch, key head, key block)
+  const int nbh = a.B * a.Hkv;
   const int wg = blockIdx.x;
   int bh, kblk;
   if ((nbh & 7) == 0) {
@@ -158,7 +156,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     bh = wg % nbh;
     kblk = wg / nbh;
   }
-  const int b = bh / a.H, h = bh - b * a.H;
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int G = a.G;  // query heads hk G .. hk G + G - 1 read this key head
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l = threadIdx.x & 63, h2 = l >> 5, l32 = l & 31;
   const bool producer = w < 4;
@@ -168,16 +167,15 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // key groups past the last key compute nothing; the last active one may
   // be ragged (its lanes past N_k are masked and store nothing)
   const bool group_active = kw < a.Nk;
-  // causal: key j is visible to query i iff j <= i + off (keys aligned to the
-  // end of the query block)
-  const int off = a.Nk - a.Nq;
+  // key j is visible to query i iff i + lo_off <= j <= i + hi_off (keys
+  // aligned to the end of the queries)
+  const int hi_off = a.Nk - a.Nq + a.wr;
+  const int lo_off = a.Nk - a.Nq - a.wl;
 
-  const size_t rs = (size_t)a.H * D;
-  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;   // Q, dO
-  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;  // K, V, dK, dV
-  const size_t rowterm_off = ((size_t)b * a.H + h) * a.Nq;
-  const float* ndrow = a.drow + rowterm_off;
-  const float* nlse2 = a.drow + (size_t)a.B * a.H * a.Nq + rowterm_off;
+  const size_t rs = (size_t)a.H * D;     // Q, dO row stride
+  const size_t rk = (size_t)a.Hkv * D;   // K, V, dK, dV row stride
+  const size_t qb_off = (size_t)b * a.Nq * rs;                   // Q, dO of batch b
+  const size_t kv_off = (size_t)b * a.Nk * rk + (size_t)hk * D;  // K, V, dK, dV
 
   // ---- per-lane LDS offsets.  Q / dO tiles use the forward kernel's
   // geometry; the swizzle XORs the chunk index, so a power-of-two chunk step
@@ -213,12 +211,6 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     const int row = p / NCH, ch = p % NCH;
     qgoff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
-  // rows 0 .. N - 1 at a stride of H d, the last ending H d - h d elements
-  // before the end of the head's span; under 2^32 bytes since B N H d < 2^31
-  // (rows past N_q read zero)
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nq * a.H - h) * D * 2);
-  const buf_rsrc qrs = make_rsrc(a.q + q_off, head_bytes);
-  const buf_rsrc grs = make_rsrc(a.dO + q_off, head_bytes);
   // buffer I (a std::integral_constant) of each kind
   auto QT = [&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value & 3;
@@ -234,7 +226,24 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   };
   auto PT = [&](auto I) __attribute__((always_inline)) { return (lds_char*)((decltype(I)::value & 1) ? p_lds1 : p_lds0); };
   auto DT = [&](auto I) __attribute__((always_inline)) { return (lds_char*)((decltype(I)::value & 1) ? ds_lds1 : ds_lds0); };
-  // copies of query block qblk into Q / dO / row-term buffer I
+  // The walk visits query blocks qlo .. qhi (set below) of each of the G
+  // query heads hk G .. hk G + G - 1 in turn.  Running state of the copies:
+  // the next block to copy (block qb_next of head hq_next), buffer resources
+  // over that head's Q and dO rows and the offset of its row terms, rebuilt
+  // only when the walk moves on to the next head.
+  int hq_next = hk * G, qb_next = 0;
+  buf_rsrc qrs, grs;
+  size_t rt_head = 0;
+  auto set_head = [&]() __attribute__((always_inline)) {
+    // query head hq_next's rows 0 .. N_q - 1 at a stride of H d, the last
+    // ending H d - hq d elements before the end of the batch's span; under
+    // 2^32 bytes since B N_q H d < 2^31 (rows past N_q read zero)
+    const uint32_t head_bytes = (uint32_t)(((size_t)a.Nq * a.H - hq_next) * D * 2);
+    qrs = make_rsrc(a.q + qb_off + (size_t)hq_next * D, head_bytes);
+    grs = make_rsrc(a.dO + qb_off + (size_t)hq_next * D, head_bytes);
+    rt_head = ((size_t)b * a.H + hq_next) * a.Nq;
+  };
+  // copies of query block qblk of the current head into Q / dO / row-term buffer I
   auto issue_q = [&](int qblk, auto I) __attribute__((always_inline)) {
     if (producer) return;
     const uint32_t soff = (uint32_t)qblk * (uint32_t)(BR * rs * 2);
@@ -253,7 +262,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     if (w == 4) {  // lanes 0-31: -L log2 e, lanes 32-63: -D of the block's rows
       // (rows past N_q repeat the last row; they are masked)
       const int row = min(qblk * BR + (l & 31), a.Nq - 1);
-      const float* src = (l < 32) ? (nlse2 + row) : (ndrow + row);
+      const size_t rt = rt_head + row;
+      const float* src = (l < 32) ? (a.drow + (size_t)a.B * a.H * a.Nq + rt) : (a.drow + rt);
       __builtin_amdgcn_global_load_lds(src, (lds_void*)RT(I), 4, 0, 0);
     }
   };
@@ -264,18 +274,42 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 
   const float c = a.c;
   const int nqb = (a.Nq + BR - 1) / BR;
-  // causal: the first query block with a row that sees a key of this block
-  const int qstart = CAUSAL ? max(0, kb - off) / BR : 0;
+  // the query blocks qlo .. qhi hold every row that sees a key of this block
+  int qlo = 0, qhi = nqb - 1;
+  if (BAND) {
+    const int i_min = max(0, kb - hi_off);
+    const int i_max = WIN ? min(a.Nq - 1, min(kb + BC, a.Nk) - 1 - lo_off) : a.Nq - 1;
+    qlo = i_min / BR;
+    qhi = i_max < i_min ? qlo - 1 : i_max / BR;
+  }
+  const int nqr = qhi - qlo + 1;
   const int key = kw + l32;
+  const int nv = max(nqr, 0) * G;  // blocks in the walk
+  qb_next = qlo;
+  set_head();
+  // qbuf[i]: the query block held in Q / dO / row-term buffer i (only ever
+  // indexed by compile-time constants, so it lives in scalar registers)
+  int qbuf[4] = {0, 0, 0, 0};
+  // copy the next block of the walk into buffer I (the producers only keep
+  // the bookkeeping) and advance the walk
+  auto issue_next = [&](auto I) __attribute__((always_inline)) {
+    qbuf[decltype(I)::value & 3] = qb_next;
+    issue_q(qb_next, I);
+    if (++qb_next > qhi) {
+      qb_next = qlo;
+      ++hq_next;
+      set_head();
+    }
+  };
   // no step when no query sees these keys (their gradients are then zero)
-  const int nsteps = qstart < nqb ? nqb - qstart + 1 : 0;
+  const int nsteps = nv > 0 ? nv + 1 : 0;
 
-  // ---- the walk.  Step t produces P^T / dS^T of block qstart + t and
-  // consumes block qstart + t - 1.  The two roles run separate loops (their
-  // registers never live at the same time) with the same barriers: s_barrier
-  // counts arrivals, so every wave passes one per step.
-  if (qstart < nqb) issue_q(qstart, IC<0>{});
-  if (qstart + 1 < nqb) issue_q(qstart + 1, IC<1>{});
+  // ---- the walk.  Step t produces P^T / dS^T of walk block t and consumes
+  // walk block t - 1.  The two roles run separate loops (their registers
+  // never live at the same time) with the same barriers: s_barrier counts
+  // arrivals, so every wave passes one per step.
+  if (0 < nv) issue_next(IC<0>{});
+  if (1 < nv) issue_next(IC<1>{});
   step_barrier();
 
   if (producer) {
@@ -284,8 +318,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) kreg[kk] = vreg[kk] = bf16x8{};
     if (group_active && key < a.Nk) {
-      const __bf16* kr = a.k + kv_off + (size_t)key * rs + 8 * h2;
-      const __bf16* vr = a.v + kv_off + (size_t)key * rs + 8 * h2;
+      const __bf16* kr = a.k + kv_off + (size_t)key * rk + 8 * h2;
+      const __bf16* vr = a.v + kv_off + (size_t)key * rk + 8 * h2;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         kreg[kk] = *(const bf16x8*)(kr + 16 * kk);
@@ -348,10 +382,10 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     // step t = T (mod 4)
     auto pstep = [&](auto T, int t, f32x16& sc, f32x16& pc, f32x16& sn, f32x16& pn) __attribute__((always_inline)) {
       constexpr int T4 = decltype(T)::value;
-      const int qi = qstart + t;
       step_barrier();
-      if (qi + 2 < nqb) issue_q(qi + 2, IC<T4 + 2>{});
-      if (!group_active || qi >= nqb) return;
+      if (t + 2 < nv) issue_next(IC<T4 + 2>{});
+      if (!group_active || t >= nv) return;
+      const int qi = qbuf[T4];
       // exp2 addends: -L log2 e of each element's row, -inf where key > query
       lds_f32x4* r4 = (lds_f32x4*)RT(T);
 #pragma unroll
@@ -360,13 +394,13 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) nlv[4 * g4 + i] = nl[i];
       }
-      // masked: key > query + off (causal), query >= N_q or key >= N_k
+      // masked: key outside the query's band, query >= N_q or key >= N_k
       const int q0 = qi * BR;
-      if ((CAUSAL && q0 + off < kw + 31) || q0 + BR > a.Nq || kw + 32 > a.Nk) {
+      if ((BAND && q0 + hi_off < kw + 31) || (WIN && q0 + BR - 1 + lo_off > kw) || q0 + BR > a.Nq || kw + 32 > a.Nk) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int qr = q0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          const bool masked = (CAUSAL && key > qr + off) || qr >= a.Nq || key >= a.Nk;
+          const bool masked = (BAND && key > qr + hi_off) || (WIN && key < qr + lo_off) || qr >= a.Nq || key >= a.Nk;
           nlv[e] = masked ? -__builtin_inff() : nlv[e];
         }
       }
@@ -401,7 +435,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   auto consume = [&](int qi, const lds_char* __restrict__ qt, const lds_char* __restrict__ gt,
                      const lds_char* __restrict__ pt, const lds_char* __restrict__ dst)
       __attribute__((always_inline)) {
-    if (CAUSAL && qi * BR + BR - 1 + off < kw) return;  // P = dS = 0 for this block
+    // P = dS = 0 for this block: every row's band misses the group's keys
+    if ((BAND && qi * BR + BR - 1 + hi_off < kw) || (WIN && qi * BR + lo_off > kw + 31)) return;
     typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
     // product i = (tq, db): A = P^T / dS^T chunks of the 16 queries of step
     // tq (queries 16 tq + 4 h2 + 0..3 and + 8), B = dO / Q columns by
@@ -438,9 +473,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   auto cstep = [&](auto T, int t) __attribute__((always_inline)) {
     constexpr int T4 = decltype(T)::value;
     step_barrier();
-    const int qi = qstart + t;
-    if (qi + 2 < nqb) issue_q(qi + 2, IC<T4 + 2>{});
-    if (group_active && t > 0) consume(qi - 1, QT(IC<T4 + 3>{}), GT(IC<T4 + 3>{}), PT(IC<T4 + 1>{}), DT(IC<T4 + 1>{}));
+    if (t + 2 < nv) issue_next(IC<T4 + 2>{});
+    if (group_active && t > 0)
+      consume(qbuf[(T4 + 3) & 3], QT(IC<T4 + 3>{}), GT(IC<T4 + 3>{}), PT(IC<T4 + 1>{}), DT(IC<T4 + 1>{}));
   };
   for (int t = 0; t < nsteps; t += 4) {
     cstep(IC<0>{}, t);
@@ -458,7 +493,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     for (int e = 0; e < 16; ++e) {
       const int kr = kw + 8 * (e >> 2) + 4 * h2 + (e & 3);
       if (kr >= a.Nk) continue;
-      const size_t o = kv_off + (size_t)kr * rs + 32 * db + l32;
+      const size_t o = kv_off + (size_t)kr * rk + 32 * db + l32;
       a.dk[o] = (__bf16)(dkacc[db][e] * scale);
       a.dv[o] = (__bf16)(dvacc[db][e]);
     }
@@ -474,8 +509,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 //        dQ^T += K^T dS^T                          (dS^T straight from the accumulators)
 //    and dQ = scale dQ^T is written once, in bf16: no accumulator in memory
 //    and no atomics.
-template <int D, int NW, int BC, bool CAUSAL>
+template <int D, int NW, int BC, bool BAND, bool WIN>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(BAND || !WIN, "a window always bounds the keys above");
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
@@ -505,8 +541,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     bh = wg % nbh;
     qi = wg / nbh;
   }
-  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int qb = BAND ? (nqb - 1 - qi) : qi;
   const int b = bh / a.H, h = bh - b * a.H;
+  const int hk = h / a.G;  // key / value head
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63, h2 = l >> 5, l32 = l & 31;
   const int q0 = qb * BR;
@@ -514,12 +551,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_active = qw < a.Nq;
   const int qrow = qw + l32;
   const bool row_valid = qrow < a.Nq;  // the last tile of rows may be ragged
-  // causal: key j is visible to query i iff j <= i + off
-  const int off = a.Nk - a.Nq;
+  // key j is visible to query i iff i + lo_off <= j <= i + hi_off
+  const int hi_off = a.Nk - a.Nq + a.wr;
+  const int lo_off = a.Nk - a.Nq - a.wl;
 
-  const size_t rs = (size_t)a.H * D;
-  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;   // Q, dO, dQ
-  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;  // K, V
+  const size_t rs = (size_t)a.H * D;     // Q, dO, dQ row stride
+  const size_t rk = (size_t)a.Hkv * D;   // K, V row stride
+  const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;    // Q, dO, dQ
+  const size_t kv_off = (size_t)b * a.Nk * rk + (size_t)hk * D;  // K, V
   const __bf16* kbase = a.k + kv_off;
   const __bf16* vbase = a.v + kv_off;
 
@@ -563,13 +602,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int p = 64 * (w + NW * i) + l;
     const int row = p / NCH, ch = p % NCH;
-    goff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    goff[i] = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.H - h) * D * 2);  // (rows past N_k read zero)
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);  // (rows past N_k read zero)
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
   const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
@@ -579,11 +618,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   const int ntiles_all = (a.Nk + BC - 1) / BC;
-  int ntiles = ntiles_all;
-  if (CAUSAL) {
-    const int last_key = min(q0 + BR, a.Nq) - 1 + off;  // last key any row here sees
+  int ntiles = ntiles_all, kt0 = 0;  // key tiles kt0 .. ntiles - 1
+  if (BAND) {
+    const int last_key = min(q0 + BR, a.Nq) - 1 + hi_off;  // last key any row here sees
     ntiles = last_key < 0 ? 0 : min(ntiles_all, last_key / BC + 1);
   }
+  if (WIN) kt0 = max(0, q0 + lo_off) / BC;                 // first key any row here sees
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -593,7 +633,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   auto compute_tile = [&](auto MASK, int kb, const lds_char* __restrict__ kt_lds,
                           const lds_char* __restrict__ vt_lds) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
-    const int lim = CAUSAL ? min(qrow + off, a.Nk - 1) : a.Nk - 1;  // last visible key
+    const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;  // last visible key
+    const int lo = qrow + lo_off;                                     // first (banded)
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       // S^T and dP^T of the 32-key sub-block: lane holds [key 8(e/4)+4h2+e%4][query l32];
@@ -622,10 +663,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int e = 0; e < 16; e += 2) {
         float p0 = fast_exp2(fmaf(sacc[e], c, nl));
         float p1 = fast_exp2(fmaf(sacc[e + 1], c, nl));
-        if constexpr (MASKED) {  // key > query + off (causal) or key >= N_k
+        if constexpr (MASKED) {  // key outside the row's band, or key >= N_k
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          p0 = (key > lim) ? 0.f : p0;
-          p1 = (key + 1 > lim) ? 0.f : p1;
+          p0 = (key > hi || (WIN && key < lo)) ? 0.f : p0;
+          p1 = (key + 1 > hi || (WIN && key + 1 < lo)) ? 0.f : p1;
         }
         dspk[e >> 1] = pack_bf16x2(p0 * (pacc[e] + ndr), p1 * (pacc[e + 1] + ndr));
       }
@@ -648,8 +689,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  // MAYMASK: whether the tile can need masking (causal diagonal tiles, or
-  // the ragged last tile); non-causal loops never instantiate the masked
+  // MAYMASK: whether the tile can need masking (tiles crossing a band edge,
+  // or the ragged last tile); unbanded loops never instantiate the masked
   // variant and take their ragged last tile after the loop
   auto tile_step = [&](auto MAYMASK, int kt, const lds_char* __restrict__ kt_lds,
                        const lds_char* __restrict__ vt_lds, lds_char* __restrict__ knext,
@@ -659,9 +700,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
     const int kb = kt * BC;
     if (!wave_active) return;
-    if (CAUSAL && kb > qw + 31 + off) return;  // whole tile in this wave's future
+    // whole tile outside every row's band in this wave
+    if ((BAND && kb > qw + 31 + hi_off) || (WIN && kb + BC - 1 < qw + lo_off)) return;
     if constexpr (decltype(MAYMASK)::value) {
-      if ((CAUSAL && kb + BC - 1 > qw + off) || kb + BC > a.Nk)
+      if ((BAND && kb + BC - 1 > qw + hi_off) || (WIN && kb < qw + 31 + lo_off) || kb + BC > a.Nk)
         compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
       else
         compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
@@ -674,14 +716,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   lds_char* K1 = (lds_char*)k_lds1;
   lds_char* V0 = (lds_char*)v_lds0;
   lds_char* V1 = (lds_char*)v_lds1;
-  constexpr auto LOOP_MASK = std::integral_constant<bool, CAUSAL>{};
-  const int nloop = (!CAUSAL && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
-  if (ntiles > 0) issue_tile(0, K0, V0);
-  for (int kt = 0; kt < nloop; kt += 2) {
+  constexpr auto LOOP_MASK = std::integral_constant<bool, BAND>{};
+  // (unbanded: kt0 = 0 and the ragged last tile is peeled)
+  const int nloop = (!BAND && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
+  if (kt0 < ntiles) issue_tile(kt0, K0, V0);
+  for (int kt = kt0; kt < nloop; kt += 2) {
     tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
     if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
   }
-  if (nloop < ntiles) {  // the ragged last tile of a non-causal walk
+  if (nloop < ntiles) {  // the ragged last tile of an unbanded walk
     if (nloop & 1)
       tile_step(std::true_type{}, nloop, K1, V1, K0, V0);
     else
@@ -703,7 +746,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND, bool WIN>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   void* args[] = {(void*)&a};
   {
@@ -714,21 +757,26 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   {
-    dim3 grid((unsigned)(a.B * a.H * ((a.Nk + 127) / 128)));
-    hipError_t e = hipLaunchKernel((const void*)bwd_main_kernel<D, CAUSAL>, grid, dim3(512), args, 0, stream);
+    dim3 grid((unsigned)(a.B * a.Hkv * ((a.Nk + 127) / 128)));
+    hipError_t e = hipLaunchKernel((const void*)bwd_main_kernel<D, BAND, WIN>, grid, dim3(512), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   {
     constexpr int NW = D == 128 ? 8 : 4;
     constexpr int BR = NW * 32;
     dim3 grid((unsigned)(a.B * a.H * ((a.Nq + BR - 1) / BR)));
-    return hipLaunchKernel((const void*)bwd_dq_kernel<D, NW, 64, CAUSAL>, grid, dim3(NW * 64), args, 0, stream);
+    return hipLaunchKernel((const void*)bwd_dq_kernel<D, NW, 64, BAND, WIN>, grid, dim3(NW * 64), args, 0, stream);
   }
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
-  return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool band, bool win, hipStream_t stream) {
+  if (win) return launch_bwd_t<D, true, true>(a, stream);
+  return band ? launch_bwd_t<D, true, false>(a, stream) : launch_bwd_t<D, false, false>(a, stream);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
+  return d == 128 ? launch_bwd_d<128>(a, band, win, stream) : launch_bwd_d<64>(a, band, win, stream);
 }
 
 }  // namespace fa

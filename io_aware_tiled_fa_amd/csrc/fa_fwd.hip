@@ -26,8 +26,12 @@
 //    running maximum is only moved (and O rescaled) when it grows by more
 //    than 2^8, which keeps the result exact (O and the sum share the stale
 //    maximum) and skips most rescale passes;
-//  * causal: key tiles after a query tile's last row are never loaded; only
-//    tiles straddling the diagonal are masked (key j visible iff j <= i);
+//  * masks: key j is visible to query i iff i + off - wl <= j <= i + off + wr
+//    (off = N_k - N_q); causal is wr = 0 with wl unbounded, a sliding window
+//    of W keys bounds wl (and, not causal, wr) by W - 1.  Key tiles outside
+//    a query tile's band are never loaded, and only tiles crossing a band
+//    edge (or the ragged end of the keys) run the masked variant;
+//  * grouped-query attention: query head h reads key / value head h / G;
 //  * workgroup order: heaviest causal query tiles first, and each XCD
 //    (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
 //    set of heads so the query tiles sharing K and V share an L2.
@@ -38,8 +42,11 @@
 
 namespace fa {
 
-template <int D, int NW, int BC, bool CAUSAL>
+// BAND: the visible keys have an upper edge (causal, or a window); WIN: they
+// also have a lower edge (a window).  Without BAND every key is visible.
+template <int D, int NW, int BC, bool BAND, bool WIN>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
+  static_assert(BAND || !WIN, "a window always bounds the keys above");
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
   constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
@@ -75,8 +82,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     bh = wg % nbh;
     qi = wg / nbh;
   }
-  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int qb = BAND ? (nqb - 1 - qi) : qi;
   const int b = bh / a.H, h = bh - b * a.H;
+  const int hk = h / a.G;  // key / value head
 
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
@@ -87,13 +95,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const bool wave_active = qw < a.Nq;
   const int qrow = qw + l32;
   const bool row_valid = qrow < a.Nq;  // the last tile of rows may be ragged
-  // causal: key j is visible to query i iff j <= i + off (keys aligned to the
-  // end of the query block); rows with i + off < 0 see no key
-  const int off = a.Nk - a.Nq;
+  // key j is visible to query i iff i + lo_off <= j <= i + hi_off; rows with
+  // i + hi_off < 0 see no key
+  const int hi_off = a.Nk - a.Nq + a.wr;
+  const int lo_off = a.Nk - a.Nq - a.wl;
 
-  const size_t rs = (size_t)a.H * D;  // elements between consecutive rows
+  const size_t rs = (size_t)a.H * D;     // elements between consecutive Q / O rows
+  const size_t rk = (size_t)a.Hkv * D;   // and K / V rows
   const size_t q_off = (size_t)b * a.Nq * rs + (size_t)h * D;
-  const size_t kv_off = (size_t)b * a.Nk * rs + (size_t)h * D;
+  const size_t kv_off = (size_t)b * a.Nk * rk + (size_t)hk * D;
   const __bf16* kbase = a.k + kv_off;
   const __bf16* vbase = a.v + kv_off;
 
@@ -149,16 +159,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int p = 64 * (w + NW * i) + l;
     const int row = p / NCH, ch = p % NCH;
-    goff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    goff[i] = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
-  // K and V of this (batch, head) as buffer resources: rows 0 .. N - 1 at a
-  // stride of H d elements, the last ending H d - h d elements before the
-  // end of the head's span; under 2^32 bytes since B N H d < 2^31
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.H - h) * D * 2);
+  // K and V of this (batch, key head) as buffer resources: rows 0 .. N_k - 1
+  // at a stride of H_kv d elements, the last ending H_kv d - hk d elements
+  // before the end of the head's span; under 2^32 bytes since B N_k H_kv d
+  // < 2^31 (rows past N_k read zero)
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
   const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rs * 2);
+    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
@@ -167,13 +178,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // ---- key tiles this workgroup visits
+  // ---- key tiles this workgroup visits: kt0 .. ntiles - 1
   const int ntiles_all = (a.Nk + BC - 1) / BC;
-  int ntiles = ntiles_all;
-  if (CAUSAL) {
-    const int last_key = min(q0 + BR, a.Nq) - 1 + off;  // last key any row here sees
+  int ntiles = ntiles_all, kt0 = 0;
+  if (BAND) {
+    const int last_key = min(q0 + BR, a.Nq) - 1 + hi_off;  // last key any row here sees
     ntiles = last_key < 0 ? 0 : min(ntiles_all, last_key / BC + 1);
   }
+  if (WIN) kt0 = max(0, q0 + lo_off) / BC;                 // first key any row here sees
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -201,18 +213,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk) sacc[sb] = mfma32(kop[kk], qop[kk], sacc[sb]);
     }
 
-    // causal mask on tiles crossing the diagonal: key > query -> -inf.  The
-    // scale factor c is never 0 (the host clamps it to a tiny positive
-    // number), so exp2(-inf * c - m) below is exactly 0 with no second mask.
+    // mask on tiles crossing a band edge: invisible key -> -inf.  The scale
+    // factor c is never 0 (the host clamps it to a tiny positive number), so
+    // exp2(-inf * c - m) below is exactly 0 with no second mask.
     if constexpr (MASKED) {
-      // key > qrow + off (causal) or key >= Nk (past the keys)
-      const int lim = CAUSAL ? min(qrow + off, a.Nk - 1) : a.Nk - 1;
+      // key outside [qrow + lo_off, qrow + hi_off], or key >= Nk (past the keys)
+      const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;
+      const int lo = qrow + lo_off;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          sacc[sb][e] = (key > lim) ? -__builtin_inff() : sacc[sb][e];
+          const bool out = WIN ? (key > hi || key < lo) : key > hi;
+          sacc[sb][e] = out ? -__builtin_inff() : sacc[sb][e];
         }
     }
 
@@ -236,9 +250,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       l_run *= alpha;
     }
 
-    // probabilities, rounded to bf16 pairs for the PV product (a row that has
-    // seen no key yet keeps m = -inf and every p = 0)
-    const float negm = (m_run == -__builtin_inff()) ? 0.f : -m_run;
+    // probabilities, rounded to bf16 pairs for the PV product.  Only a masked
+    // tile can leave a row without a key so far (m = -inf, every p = 0); after
+    // an unmasked tile m is finite.
+    const float negm = (MASKED && m_run == -__builtin_inff()) ? 0.f : -m_run;
     uint32_t pk[NSB][8];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
@@ -271,10 +286,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
 
   // one key tile: wait for its copies, start the next tile's copies into
   // the other buffer, then compute on this one.  MAYMASK (std::true_type /
-  // std::false_type) says whether the tile can need masking: causal tiles
-  // crossing a wave's diagonal, or the ragged last tile (keys past N_k, which
-  // the copy read as zeros).  Non-causal loops never instantiate the masked
-  // variant; their ragged last tile is peeled off the loop.
+  // std::false_type) says whether the tile can need masking: tiles crossing
+  // a band edge of the wave's rows, or the ragged last tile (keys past N_k,
+  // which the copy read as zeros).  Unbanded loops never instantiate the
+  // masked variant; their ragged last tile is peeled off the loop.
   auto tile_step = [&](auto MAYMASK, int kt, const lds_char* kt_lds, const lds_char* vt_lds,
                        lds_char* knext, lds_char* vnext) __attribute__((always_inline)) {
     wait_vmem();
@@ -282,9 +297,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     if (kt + 1 < ntiles) issue_tile(kt + 1, knext, vnext);
     if (!wave_active) return;
     const int kb = kt * BC;
-    if (CAUSAL && kb > qw + 31 + off) return;  // whole tile in this wave's future
+    // whole tile outside every row's band in this wave
+    if ((BAND && kb > qw + 31 + hi_off) || (WIN && kb + BC - 1 < qw + lo_off)) return;
     if constexpr (decltype(MAYMASK)::value) {
-      if ((CAUSAL && kb + BC - 1 > qw + off) || kb + BC > a.Nk)
+      if ((BAND && kb + BC - 1 > qw + hi_off) || (WIN && kb < qw + 31 + lo_off) || kb + BC > a.Nk)
         compute_tile(std::true_type{}, kb, kt_lds, vt_lds);
       else
         compute_tile(std::false_type{}, kb, kt_lds, vt_lds);
@@ -297,14 +313,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   lds_char* K1 = (lds_char*)k_lds1;
   lds_char* V0 = (lds_char*)v_lds0;
   lds_char* V1 = (lds_char*)v_lds1;
-  constexpr auto LOOP_MASK = std::integral_constant<bool, CAUSAL>{};
-  const int nloop = (!CAUSAL && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
-  if (ntiles > 0) issue_tile(0, K0, V0);
-  for (int kt = 0; kt < nloop; kt += 2) {
+  constexpr auto LOOP_MASK = std::integral_constant<bool, BAND>{};
+  // (unbanded: kt0 = 0 and the ragged last tile is peeled)
+  const int nloop = (!BAND && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
+  if (kt0 < ntiles) issue_tile(kt0, K0, V0);
+  for (int kt = kt0; kt < nloop; kt += 2) {
     tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
     if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
   }
-  if (nloop < ntiles) {  // the ragged last tile of a non-causal walk
+  if (nloop < ntiles) {  // the ragged last tile of an unbanded walk
     if (nloop & 1)
       tile_step(std::true_type{}, nloop, K1, V1, K0, V0);
     else
@@ -331,20 +348,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     a.lse[((size_t)b * a.H + h) * a.Nq + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -__builtin_inff();
 }
 
-template <int D, int NW, int BC, bool CAUSAL>
+template <int D, int NW, int BC, bool BAND, bool WIN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32;
   const int nqb = (a.Nq + BR - 1) / BR;
   dim3 grid((unsigned)(a.B * a.H * nqb));
   dim3 block(NW * 64);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, CAUSAL>, grid, block, args, 0, stream);
+  return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, BAND, WIN>, grid, block, args, 0, stream);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 128)
-    return causal ? launch_fwd_t<128, 8, 64, true>(a, stream) : launch_fwd_t<128, 8, 64, false>(a, stream);
-  return causal ? launch_fwd_t<64, 4, 64, true>(a, stream) : launch_fwd_t<64, 4, 64, false>(a, stream);
+template <int D, int NW, int BC>
+static hipError_t launch_fwd_d(const FwdArgs& a, bool band, bool win, hipStream_t stream) {
+  if (win) return launch_fwd_t<D, NW, BC, true, true>(a, stream);
+  return band ? launch_fwd_t<D, NW, BC, true, false>(a, stream) : launch_fwd_t<D, NW, BC, false, false>(a, stream);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
+  return d == 128 ? launch_fwd_d<128, 8, 64>(a, band, win, stream) : launch_fwd_d<64, 4, 64>(a, band, win, stream);
 }
 
 }  // namespace fa

@@ -12,7 +12,8 @@ normal tensors stand in for real activations):
 * generator: ``numpy.random.default_rng(seed)`` (PCG64), seed 0 by default;
 * tensors drawn in the order Q, K, V, then dO when a backward input is asked
   for, each as ``standard_normal((B, N, H, d), dtype=float32)`` (K and V use
-  ``N_k`` rows when it differs from ``N``);
+  ``N_k`` rows when it differs from ``N``, and ``H_kv`` heads when it
+  differs from ``H``);
 * optional "peaked rows": after all tensors are drawn, for every (b, h) in
   row-major order, ``round(fraction * N)`` distinct query positions are chosen
   with ``rng.choice(N, size, replace=False)`` and those Q rows are multiplied
@@ -66,6 +67,7 @@ class AttentionInputs:
     d: int
     N_k: int
     seed: int
+    H_kv: int
     q_bits: np.ndarray
     k_bits: np.ndarray
     v_bits: np.ndarray
@@ -100,16 +102,18 @@ class AttentionInputs:
 
 
 def make_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0,
-                N_k: Optional[int] = None, with_do: bool = False,
+                N_k: Optional[int] = None, H_kv: Optional[int] = None, with_do: bool = False,
                 peaked_fraction: float = 0.0,
                 peak_factor: float = 4.0) -> AttentionInputs:
     """Draw Q, K, V (and dO) as described in the module docstring."""
     if N_k is None:
         N_k = N
+    if H_kv is None:
+        H_kv = H
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, N, H, d), dtype=np.float32)
-    k = rng.standard_normal((B, N_k, H, d), dtype=np.float32)
-    v = rng.standard_normal((B, N_k, H, d), dtype=np.float32)
+    k = rng.standard_normal((B, N_k, H_kv, d), dtype=np.float32)
+    v = rng.standard_normal((B, N_k, H_kv, d), dtype=np.float32)
     do = rng.standard_normal((B, N, H, d), dtype=np.float32) if with_do else None
     peaked = None
     if peaked_fraction > 0.0:
@@ -121,7 +125,7 @@ def make_inputs(B: int, H: int, N: int, d: int, *, seed: int = 0,
                 peaked[b, h] = rows
                 q[b, rows, h, :] *= np.float32(peak_factor)
     return AttentionInputs(
-        B=B, H=H, N=N, d=d, N_k=N_k, seed=seed,
+        B=B, H=H, N=N, d=d, N_k=N_k, seed=seed, H_kv=H_kv,
         q_bits=bf16_bits_from_f32(q), k_bits=bf16_bits_from_f32(k),
         v_bits=bf16_bits_from_f32(v),
         do_bits=None if do is None else bf16_bits_from_f32(do),

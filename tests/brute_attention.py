@@ -12,17 +12,22 @@ from __future__ import annotations
 import math
 
 
-def _visible(i, j, n_q, n_k, causal):
-    return (not causal) or (j <= i + (n_k - n_q))
+def _visible(i, j, n_q, n_k, causal, window=0):
+    pos = i + (n_k - n_q)  # the query's position among the keys
+    if causal and j > pos:
+        return False
+    if window > 0 and abs(pos - j) >= window:
+        return False
+    return True
 
 
-def brute_forward(q, k, v, scale, causal):
+def brute_forward(q, k, v, scale, causal, window=0):
     """q [n_q][d], k [n_k][d], v [n_k][dv] nested lists -> (o, lse)."""
     n_q, n_k = len(q), len(k)
     d, dv = len(q[0]), len(v[0])
     o, lse = [], []
     for i in range(n_q):
-        vis = [j for j in range(n_k) if _visible(i, j, n_q, n_k, causal)]
+        vis = [j for j in range(n_k) if _visible(i, j, n_q, n_k, causal, window)]
         if not vis:
             o.append([0.0] * dv)
             lse.append(-math.inf)
@@ -36,7 +41,7 @@ def brute_forward(q, k, v, scale, causal):
     return o, lse
 
 
-def brute_backward(q, k, v, do, scale, causal):
+def brute_backward(q, k, v, do, scale, causal, window=0):
     """Gradients of sum(O * dO) with respect to q, k, v (nested lists)."""
     n_q, n_k = len(q), len(k)
     d, dv = len(q[0]), len(v[0])
@@ -44,7 +49,7 @@ def brute_backward(q, k, v, do, scale, causal):
     dk_terms = [[[] for _ in range(d)] for _ in range(n_k)]
     dv_terms = [[[] for _ in range(dv)] for _ in range(n_k)]
     for i in range(n_q):
-        vis = [j for j in range(n_k) if _visible(i, j, n_q, n_k, causal)]
+        vis = [j for j in range(n_k) if _visible(i, j, n_q, n_k, causal, window)]
         if not vis:
             continue
         s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis}

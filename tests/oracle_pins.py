@@ -370,6 +370,126 @@ def pin_gradient_identities(orc):
         _close(dv3, 3.0 * dv - dv2, 1e-12, "dV linear in dO")
 
 
+# --------------------------------------------------------------------------
+# sliding window and grouped-query attention
+# --------------------------------------------------------------------------
+
+def pin_window_closed_forms(orc):
+    """W = 1: every row sees only its own position, so O_i = V_i', LSE_i =
+    s_ii', dV = dO scattered to those keys, dQ = dK = 0 (a one-key softmax is
+    constant).  W = 2 causal: row i sees keys i - 1 and i, so O_i = sig V_i +
+    (1 - sig) V_{i-1} with sig = 1 / (1 + exp(s_i,i-1 - s_ii)).  A window
+    wider than every distance changes nothing."""
+    rng = np.random.default_rng(51)
+    B, H, d, scale = 1, 2, 4, 0.7
+    for (n_q, n_k, causal) in ((9, 9, True), (9, 9, False), (4, 9, True), (4, 9, False)):
+        q, do = _rand(rng, B, n_q, H, d), _rand(rng, B, n_q, H, d)
+        k, v = _rand(rng, B, n_k, H, d), _rand(rng, B, n_k, H, d)
+        pos = np.arange(n_q) + (n_k - n_q)
+        o, lse = orc.attention_forward(q, k, v, scale, causal, window=1)
+        _close(o, v[:, pos], 1e-14, "W=1: O = V at the own position")
+        _close(lse, scale * np.einsum("bihc,bihc->bhi", q, k[:, pos]), 1e-13, "W=1: LSE = own score")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, scale, causal, window=1)
+        want_dv = np.zeros_like(v)
+        want_dv[:, pos] = do
+        _close(dv, want_dv, 1e-14, "W=1: dV = dO at the own position")
+        _close(dq, np.zeros_like(dq), 1e-14, "W=1: dQ = 0")
+        _close(dk, np.zeros_like(dk), 1e-14, "W=1: dK = 0")
+        o_w, lse_w = orc.attention_forward(q, k, v, scale, causal, window=n_q + n_k)
+        o_f, lse_f = orc.attention_forward(q, k, v, scale, causal)
+        _close(o_w, o_f, 1e-15, "wide window = no window (O)")
+        _close(lse_w, lse_f, 1e-15, "wide window = no window (LSE)")
+    n = 7
+    q, k, v = _rand(rng, 1, n, 1, d), _rand(rng, 1, n, 1, d), _rand(rng, 1, n, 1, d)
+    o, _ = orc.attention_forward(q, k, v, scale, True, window=2)
+    s_self = scale * np.sum(q[0, 1:, 0] * k[0, 1:, 0], axis=1)
+    s_prev = scale * np.sum(q[0, 1:, 0] * k[0, :-1, 0], axis=1)
+    sig = 1.0 / (1.0 + np.exp(s_prev - s_self))
+    want = sig[:, None] * v[0, 1:, 0] + (1.0 - sig[:, None]) * v[0, :-1, 0]
+    _close(o[0, 1:, 0], want, 1e-13, "W=2 causal: two-key softmax")
+    _close(o[0, 0, 0], v[0, 0, 0], 1e-14, "W=2 causal: first row sees one key")
+
+
+def pin_brute_force_window(orc):
+    """Pure-Python loops with a window agree with the oracle to 1e-12,
+    forward and backward, square and cross shapes."""
+    rng = np.random.default_rng(52)
+    for (n_q, n_k, d, causal, window) in ((12, 12, 3, True, 3), (12, 12, 3, False, 3), (5, 13, 4, True, 4),
+                                          (13, 5, 2, False, 2), (10, 10, 4, True, 1), (8, 11, 3, False, 6)):
+        q, do = _rand(rng, 1, n_q, 1, d), _rand(rng, 1, n_q, 1, d)
+        k, v = _rand(rng, 1, n_k, 1, d), _rand(rng, 1, n_k, 1, d)
+        o, lse = orc.attention_forward(q, k, v, 0.8, causal, window=window)
+        bo, blse = brute_forward(q[0, :, 0].tolist(), k[0, :, 0].tolist(), v[0, :, 0].tolist(), 0.8, causal,
+                                 window)
+        tag = f"{n_q}x{n_k} causal={causal} W={window}"
+        _close(o[0, :, 0], np.array(bo), 1e-12, f"brute O {tag}")
+        want = np.array(blse)
+        assert np.array_equal(np.isinf(lse[0, 0]), np.isinf(want)), tag
+        fin = np.isfinite(want)
+        _close(lse[0, 0][fin], want[fin], 1e-12, f"brute LSE {tag}")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.8, causal, window=window)
+        bq, bk, bv = brute_backward(q[0, :, 0].tolist(), k[0, :, 0].tolist(), v[0, :, 0].tolist(),
+                                    do[0, :, 0].tolist(), 0.8, causal, window)
+        _close(dq[0, :, 0], np.array(bq), 1e-12, f"brute dQ {tag}")
+        _close(dk[0, :, 0], np.array(bk), 1e-12, f"brute dK {tag}")
+        _close(dv[0, :, 0], np.array(bv), 1e-12, f"brute dV {tag}")
+
+
+def pin_torch_float64_gqa_window(orc):
+    """torch CPU float64 attention with enable_gqa (query heads grouped over
+    fewer K/V heads) and an explicit band mask, plus autograd, agrees to
+    1e-12, including dK / dV summed over each group."""
+    import torch
+
+    rng = np.random.default_rng(53)
+    for (H, H_kv, n_q, n_k, causal, window) in ((6, 2, 21, 21, True, 0), (8, 1, 17, 30, False, 0),
+                                                (4, 2, 25, 25, True, 7), (4, 4, 19, 33, False, 5),
+                                                (6, 3, 25, 19, False, 8)):
+        B, d = 2, 8
+        q, do = _rand(rng, B, n_q, H, d), _rand(rng, B, n_q, H, d)
+        k, v = _rand(rng, B, n_k, H_kv, d), _rand(rng, B, n_k, H_kv, d)
+        tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), dtype=torch.float64, requires_grad=True)
+                      for x in (q, k, v))
+        pos = torch.arange(n_q)[:, None] + (n_k - n_q)
+        j = torch.arange(n_k)[None, :]
+        mask = torch.ones(n_q, n_k, dtype=torch.bool)
+        if causal:
+            mask &= j <= pos
+        if window:
+            mask &= (pos - j).abs() < window
+        assert bool(mask.any(dim=1).all()), "every row must see a key (torch gives NaN otherwise)"
+        to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.5,
+                                                              enable_gqa=True)
+        to.backward(torch.tensor(do.transpose(0, 2, 1, 3), dtype=torch.float64))
+        tag = f"H={H}/{H_kv} {n_q}x{n_k} causal={causal} W={window}"
+        o, _ = orc.attention_forward(q, k, v, 0.5, causal, window=window)
+        _close(o, to.detach().numpy().transpose(0, 2, 1, 3), 1e-12, f"torch O {tag}")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.5, causal, window=window)
+        for name, mine, ref in (("dQ", dq, tq.grad), ("dK", dk, tk.grad), ("dV", dv, tv.grad)):
+            _close(mine, ref.numpy().transpose(0, 2, 1, 3), 1e-12, f"torch {name} {tag}")
+
+
+def pin_gqa_is_repeated_heads(orc):
+    """Grouped-query attention equals multi-head attention on K / V heads
+    repeated over each group, and the shared heads' gradients are the sums
+    of the repeated heads' gradients."""
+    rng = np.random.default_rng(54)
+    B, H, H_kv, n, d = 2, 6, 2, 11, 4
+    q, do = _rand(rng, B, n, H, d), _rand(rng, B, n, H, d)
+    k, v = _rand(rng, B, n, H_kv, d), _rand(rng, B, n, H_kv, d)
+    kr, vr = np.repeat(k, H // H_kv, axis=2), np.repeat(v, H // H_kv, axis=2)
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.6, causal)
+        o_r, lse_r = orc.attention_forward(q, kr, vr, 0.6, causal)
+        _close(o, o_r, 1e-15, "GQA O = repeated-head O")
+        _close(lse, lse_r, 1e-15, "GQA LSE = repeated-head LSE")
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.6, causal)
+        dq_r, dk_r, dv_r = orc.attention_backward(q, kr, vr, do, 0.6, causal)
+        _close(dq, dq_r, 1e-15, "GQA dQ")
+        _close(dk, dk_r.reshape(B, n, H_kv, H // H_kv, d).sum(axis=3), 1e-14, "GQA dK = group sum")
+        _close(dv, dv_r.reshape(B, n, H_kv, H // H_kv, d).sum(axis=3), 1e-14, "GQA dV = group sum")
+
+
 ALL_PINS = [
     pin_constant_v,
     pin_uniform_scores,
@@ -388,6 +508,10 @@ ALL_PINS = [
     pin_torch_float64,
     pin_torch_float64_cross,
     pin_suffix_queries,
+    pin_window_closed_forms,
+    pin_brute_force_window,
+    pin_torch_float64_gqa_window,
+    pin_gqa_is_repeated_heads,
     pin_finite_differences,
     pin_gradient_identities,
 ]

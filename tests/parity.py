@@ -111,14 +111,23 @@ def sample_rows(n: int, count: int, rng: np.random.Generator, extra=()) -> np.nd
 U_BF16 = 2.0 ** -8
 
 
-def _probabilities(q, k, scale, causal):
-    """Softmax rows for the bounds; under the causal mask the keys are aligned
-    to the end of the queries, and a row that sees no key is all zero."""
-    s = scale * (q @ k.T)
-    n_q, n_k = s.shape
+def _visible(n_q, n_k, causal, window):
+    """Keys aligned to the end of the queries; causal and window as in the
+    library's conventions (written out here, independent of the oracle)."""
+    pos = np.arange(n_q)[:, None] + (n_k - n_q)
+    j = np.arange(n_k)[None, :]
+    vis = np.ones((n_q, n_k), dtype=bool)
     if causal:
-        vis = np.arange(n_k)[None, :] <= np.arange(n_q)[:, None] + (n_k - n_q)
-        s = np.where(vis, s, -np.inf)
+        vis &= j <= pos
+    if window > 0:
+        vis &= np.abs(pos - j) < window
+    return vis
+
+
+def _probabilities(q, k, scale, causal, window=0):
+    """Softmax rows for the bounds; a row that sees no key is all zero."""
+    s = scale * (q @ k.T)
+    s = np.where(_visible(s.shape[0], s.shape[1], causal, window), s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     m = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m)
@@ -126,31 +135,37 @@ def _probabilities(q, k, scale, causal):
     return e / np.where(tot > 0, tot, 1.0)
 
 
-def forward_error_bound(q, k, v, scale, causal):
-    """Per-element bound for O, layout [B, N, H, d]."""
+def forward_error_bound(q, k, v, scale, causal, window=0):
+    """Per-element bound for O, layout [B, N, H, d] (K, V may have fewer heads)."""
     B, N, H, d = q.shape
+    G = H // k.shape[2]
     out = np.empty((B, N, H, v.shape[3]))
     for b in range(B):
         for h in range(H):
-            p = _probabilities(q[b, :, h].astype(np.float64), k[b, :, h].astype(np.float64), scale, causal)
-            out[b, :, h] = 2 * U_BF16 * (p @ np.abs(v[b, :, h].astype(np.float64)))
+            p = _probabilities(q[b, :, h].astype(np.float64), k[b, :, h // G].astype(np.float64), scale, causal,
+                               window)
+            out[b, :, h] = 2 * U_BF16 * (p @ np.abs(v[b, :, h // G].astype(np.float64)))
     return out
 
 
-def backward_error_bound(q, k, v, do, o_ref, scale, causal):
-    """Per-element bounds for (dQ, dK, dV), layouts like the inputs."""
+def backward_error_bound(q, k, v, do, o_ref, scale, causal, window=0):
+    """Per-element bounds for (dQ, dK, dV), layouts like the inputs; a K / V
+    head shared by several query heads adds up their bounds."""
     B, N, H, d = q.shape
-    n_k = k.shape[1]
-    bq, bk, bv = np.empty((B, N, H, d)), np.empty((B, n_k, H, d)), np.empty((B, n_k, H, d))
+    n_k, H_kv = k.shape[1], k.shape[2]
+    G = H // H_kv
+    bq = np.empty((B, N, H, d))
+    bk, bv = np.zeros((B, n_k, H_kv, d)), np.zeros((B, n_k, H_kv, d))
     for b in range(B):
         for h in range(H):
-            qh, kh, vh, gh = (x[b, :, h].astype(np.float64) for x in (q, k, v, do))
-            p = _probabilities(qh, kh, scale, causal)
+            qh, gh = q[b, :, h].astype(np.float64), do[b, :, h].astype(np.float64)
+            kh, vh = k[b, :, h // G].astype(np.float64), v[b, :, h // G].astype(np.float64)
+            p = _probabilities(qh, kh, scale, causal, window)
             dp = gh @ vh.T
             dd = U_BF16 * np.abs(gh * o_ref[b, :, h]).sum(axis=1, keepdims=True)
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dds = p * dd + U_BF16 * np.abs(ds)
             bq[b, :, h] = abs(scale) * (dds @ np.abs(kh))
-            bk[b, :, h] = abs(scale) * (dds.T @ np.abs(qh))
-            bv[b, :, h] = U_BF16 * (p.T @ np.abs(gh))
+            bk[b, :, h // G] += abs(scale) * (dds.T @ np.abs(qh))
+            bv[b, :, h // G] += U_BF16 * (p.T @ np.abs(gh))
     return bq, bk, bv

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_qk", "fa_bwd", "fa_bwd_qk", "fa_bwd_workspace_size",
-         "fa_status_string", "fa_version"])
+        ["fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_bwd", "fa_bwd_qk", "fa_bwd_ex",
+         "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -134,6 +134,45 @@ def test_cross_shape_validation(lib):
     big = lib.fa_bwd_workspace_size(1, 1, 512, 64)
     assert bwd_qk(lib, Nq=512, Nk=64, ws_bytes=lib.fa_bwd_workspace_size(1, 1, 64, 64)) == -6
     assert bwd_qk(lib, Nq=512, Nk=64, ws_bytes=big, scale=float("nan")) == -7
+
+
+def fwd_ex(lib, H=4, Hkv=2, Nq=128, Nk=128, window=0, B=1, d=64, scale=0.125, causal=1, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4])
+    p.update(ptrs)
+    return lib.fa_fwd_ex(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, Hkv, Nq, Nk, d, scale, causal,
+                         window, None)
+
+
+def bwd_ex(lib, H=4, Hkv=2, Nq=128, Nk=128, window=0, B=1, d=64, scale=0.125, causal=1, ws=P[9],
+           ws_bytes=None, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8])
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(B, H, Nq, d)
+    return lib.fa_bwd_ex(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                         B, H, Hkv, Nq, Nk, d, scale, causal, window, ws, ws_bytes, None)
+
+
+def test_grouped_heads_and_window_validation(lib):
+    nan = float("nan")
+    for call in (fwd_ex, bwd_ex):
+        assert call(lib, Hkv=0) == -2
+        assert call(lib, Hkv=-1) == -2
+        assert call(lib, H=6, Hkv=4) == -2                  # 6 query heads over 4 K/V heads
+        assert call(lib, H=4, Hkv=8) == -2
+        assert call(lib, window=-1) == -9
+        assert call(lib, causal=0, window=-3) == -9
+        assert call(lib, H=8, Hkv=1, scale=nan) == -7       # multi-query: valid shape
+        assert call(lib, H=8, Hkv=8, window=1, scale=nan) == -7
+        assert call(lib, H=32, Hkv=4, Nq=77, Nk=300, window=4096, causal=0, scale=nan) == -7
+    # K / V are sized by H_kv: a K with more than 2^31 elements is refused even
+    # when Q is small, and one under it is accepted
+    assert fwd_ex(lib, H=16, Hkv=16, Nq=1, Nk=2 ** 20, d=128) == -2
+    assert fwd_ex(lib, H=16, Hkv=1, Nq=1, Nk=2 ** 20, d=128, scale=nan) == -7
+    # overlap checks use the K / V extent: B N_k H_kv d bf16 = 16 KiB here
+    assert fwd_ex(lib, H=4, Hkv=1, o=P[1] + 16384 - 256) == -9
+    assert fwd_ex(lib, H=4, Hkv=1, o=P[1] + 16384, scale=nan) == -7
+    assert bwd_ex(lib, H=4, Hkv=1, dk=P[2] + 16384 - 256) == -9
 
 
 def test_workspace_size(lib):

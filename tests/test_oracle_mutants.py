@@ -17,14 +17,17 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "attent
 
 MUTANTS = {
     "scale dropped from scores": ("return float(scale) * (q @ k.T)", "return (q @ k.T)"),
-    "causal mask off by one": ("return j <= (rows[:, None] + (n_k - n_q))",
-                               "return j < (rows[:, None] + (n_k - n_q))"),
-    "causal mask transposed": ("return j <= (rows[:, None] + (n_k - n_q))",
-                               "return j >= (rows[:, None] + (n_k - n_q))"),
-    "causal keys aligned to the start": ("return j <= (rows[:, None] + (n_k - n_q))",
-                                         "return j <= rows[:, None]"),
-    "causal offset sign reversed": ("return j <= (rows[:, None] + (n_k - n_q))",
-                                    "return j <= (rows[:, None] + (n_q - n_k))"),
+    "causal mask off by one": ("vis &= j <= pos", "vis &= j < pos"),
+    "causal mask transposed": ("vis &= j <= pos", "vis &= j >= pos"),
+    "causal keys aligned to the start": ("pos = rows[:, None] + (n_k - n_q)", "pos = rows[:, None] + 0"),
+    "causal offset sign reversed": ("pos = rows[:, None] + (n_k - n_q)", "pos = rows[:, None] + (n_q - n_k)"),
+    "window one key too wide": ("vis &= np.abs(pos - j) < window", "vis &= np.abs(pos - j) <= window"),
+    "window one-sided": ("vis &= np.abs(pos - j) < window", "vis &= (pos - j) < window"),
+    "window ignored by the backward": ("visible_mask(q.shape[0], k.shape[0], causal, None, window)",
+                                       "visible_mask(q.shape[0], k.shape[0], causal, None, 0)"),
+    "query heads spread round-robin over K/V heads": ("return h // (n_heads // n_kv_heads)",
+                                                      "return h % n_kv_heads"),
+    "shared K/V gradient overwritten, not summed": ("dk[b, :, hk, :] += gk", "dk[b, :, hk, :] = gk"),
     "softmax summed over the wrong axis": ("l = e.sum(axis=1)", "l = e.sum(axis=0)"),
     "max shift not undone in LSE": ("m + np.log(np.where(l > 0, l, 1.0))",
                                     "np.log(np.where(l > 0, l, 1.0))"),
