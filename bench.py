@@ -8,6 +8,11 @@ tensors already resident in HBM.  Useful flops: forward 4 B H N^2 d, halved
 when causal; backward 2.5x the forward of its batch (five matrix products
 per tile pair, the recomputation of the scores included).
 
+The same line carries a "next" object: one timed configuration for each of
+the extensions past the five workloads (cross attention, grouped K/V heads,
+a sliding window, split-KV decoding), each against its own roofline
+(``--no-next`` skips them).
+
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
 GPU only (attention heads are independent, see the design notes for how
 it would shard).
@@ -52,6 +57,22 @@ def fwd_algorithmic_bytes(c) -> float:
     """HBM bytes the forward must move: read Q, K, V, write O (bf16), write LSE (fp32)."""
     t = c["B"] * c["N"] * c["H"] * c["d"] * 2
     return 4 * t + c["B"] * c["H"] * c["N"] * 4
+
+
+def visible_pairs(Nq: int, Nk: int, causal: bool, window: int = 0) -> int:
+    """Query-key pairs inside the mask (keys aligned to the end of the
+    queries; a window W keeps |i + N_k - N_q - j| < W)."""
+    import numpy as np
+
+    pos = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    hi = np.full(Nq, Nk - 1, dtype=np.int64)
+    lo = np.zeros(Nq, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, pos)
+    if window > 0:
+        hi = np.minimum(hi, pos + window - 1)
+        lo = np.maximum(lo, pos - window + 1)
+    return int(np.maximum(hi - lo + 1, 0).sum())
 
 
 def kernel_source_hash() -> str:
@@ -190,6 +211,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the extension configurations")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
@@ -315,7 +337,7 @@ def main(argv=None):
             "ms_p90": round(pct(bwd_ms, 0.9), 4), "useful_tflop": round(bf / 1e12, 4),
         },
         "roofline": {
-            "kernel": "fwd_kernel<128,8,64,true> (8 waves, 256 query rows per workgroup, 64-key tiles)",
+            "kernel": "fwd_kernel<128,8,64,true,false> (8 waves, 256 query rows per workgroup, 64-key tiles)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -328,11 +350,90 @@ def main(argv=None):
         "cpu_baseline": None,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_next:
+        print("# extension configurations", file=sys.stderr, flush=True)
+        rec["next"] = measure_next(binding, torch, dev)
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(fin, bin_, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def measure_next(binding, torch, dev, reps: int = 7) -> dict:
+    """One configuration per extension, median of ``reps`` timed launches
+    after one untimed launch; inputs seeded N(0,1) bf16 made on the GPU."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=torch.bfloat16, generator=g)
+
+    def timed(call):
+        call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    out = {}
+
+    def mfma_entry(name, desc, flops, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"config": desc, "ms_median": round(ms, 4), "tflops": round(tf, 2),
+                     "bound": "mfma", "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # cross attention: 4096 queries at the end of a 16384-key context
+    B, H, Nq, Nk, d = 1, 32, 4096, 16384, 128
+    q, k, v = rnd(B, Nq, H, d), rnd(B, Nk, H, d), rnd(B, Nk, H, d)
+    fl = 4.0 * B * H * d * visible_pairs(Nq, Nk, True)
+    mfma_entry("fwd_cross_b1_h32_nq4096_nk16384_d128_causal", "fa_fwd_qk", fl,
+               timed(lambda: binding.forward(q, k, v, causal=True)))
+    del q, k, v
+
+    # grouped K/V heads, forward and backward
+    B, H, Hkv, N, d = 2, 32, 8, 8192, 128
+    q, do = rnd(B, N, H, d), rnd(B, N, H, d)
+    k, v = rnd(B, N, Hkv, d), rnd(B, N, Hkv, d)
+    fl = 4.0 * B * H * d * visible_pairs(N, N, True)
+    mfma_entry("fwd_gqa_b2_h32_hkv8_n8192_d128_causal", "fa_fwd_ex", fl,
+               timed(lambda: binding.forward(q, k, v, causal=True)))
+    o, lse = binding.forward(q, k, v, causal=True)
+    ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    mfma_entry("bwd_gqa_b2_h32_hkv8_n8192_d128_causal", "fa_bwd_ex", 2.5 * fl,
+               timed(lambda: binding.backward(q, k, v, o, lse, do, causal=True, workspace=ws)))
+    del q, k, v, do, o, lse, ws
+
+    # sliding window of 4096 keys over a 32768-token sequence
+    B, H, N, d, W = 1, 32, 32768, 128, 4096
+    q, k, v = rnd(B, N, H, d), rnd(B, N, H, d), rnd(B, N, H, d)
+    fl = 4.0 * B * H * d * visible_pairs(N, N, True, W)
+    mfma_entry("fwd_window4096_b1_h32_n32768_d128_causal", "fa_fwd_ex", fl,
+               timed(lambda: binding.forward(q, k, v, causal=True, window=W)))
+    del q, k, v
+
+    # split-KV decoding: one new token per sequence against a 32768-token cache
+    B, H, Hkv, Nq, Nk, d = 8, 32, 8, 1, 32768, 128
+    q, k, v = rnd(B, Nq, H, d), rnd(B, Nk, Hkv, d), rnd(B, Nk, Hkv, d)
+    need = binding.load_library().fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, 1, 0, 0)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ms = timed(lambda: binding.decode(q, k, v, causal=True, out=o, lse=lse, workspace=ws))
+    byts = 2 * B * Nk * Hkv * d * 2 + 2 * B * Nq * H * d * 2 + B * H * Nq * 4
+    gbs = byts / (ms * 1e-3) / 1e9
+    out["decode_b8_h32_hkv8_nq1_nk32768_d128"] = {
+        "config": "fa_fwd_decode", "ms_median": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
+        "frac_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": byts}
+    ms_f = timed(lambda: binding.forward(q, k, v, causal=True, out=o, lse=lse))
+    out["decode_b8_h32_hkv8_nq1_nk32768_d128"]["general_forward_ms"] = round(ms_f, 4)
+    return out
 
 
 if __name__ == "__main__":

@@ -75,7 +75,8 @@ typedef enum {
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required         */
   FA_ERR_SCALE = -7,      /* scale is NaN or infinite                        */
   FA_ERR_LAUNCH = -8,     /* the HIP launch reported an error                */
-  FA_ERR_ARG = -9         /* causal not 0/1, window < 0, or outputs alias    */
+  FA_ERR_ARG = -9         /* causal not 0/1, window or num_splits < 0, or an */
+                          /* output aliases an input or another output       */
 } fa_status;
 
 /*
@@ -113,6 +114,30 @@ fa_status fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float*
 fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
                     void* stream);
+
+/*
+ * Forward pass for decoding: few query rows against a long key sequence.
+ * Decoding is bound by reading the key / value cache ("What Is Flash
+ * Attention? The Real Speed and Memory Gains, Explained", bestllmfor.com,
+ * "What you actually gain on a local machine"), so this entry point splits
+ * the keys over several workgroups, packs the H / H_kv query heads that
+ * share a key / value head into one tile (each key and value is read once
+ * per group), and merges the splits by their log-sum-exp.  Arguments and
+ * results are those of fa_fwd_ex, plus:
+ *   num_splits : key splits per (batch, key head); 0 lets the library
+ *                choose (enough workgroups to fill the GPU).
+ *   workspace  : device memory of at least fa_decode_workspace_size(...)
+ *                bytes (same shape arguments and num_splits), 256-byte
+ *                aligned, caller-owned, overwritten; may be NULL when that
+ *                size is 0 (a single split).
+ * When (H / H_kv) * N_q exceeds 32 rows the tile cannot be packed and the
+ * call runs fa_fwd_ex instead (the workspace size is then 0).
+ */
+size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int causal, int window,
+                                int num_splits);
+fa_status fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
+                        int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape: two float32

@@ -26,8 +26,8 @@ FA_STATUS = {
     -4: "FA_ERR_SEQLEN", -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE",
     -7: "FA_ERR_SCALE", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_bwd", "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size",
-            "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_fwd_decode", "fa_decode_workspace_size", "fa_bwd",
+            "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -60,6 +60,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_ex.restype = i
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_fwd_decode.restype = i
+    lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -138,6 +142,35 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None, window
                        B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(window),
                        _stream_ptr(q.device, stream))
     _check(lib, "fa_fwd_ex", st)
+    return out, lse
+
+
+def decode(q, k, v, causal: bool = False, scale: Optional[float] = None, window: int = 0,
+           num_splits: int = 0, out=None, lse=None, workspace=None, stream=None) -> Tuple[object, object]:
+    """O, LSE = fa_fwd_decode(Q, K, V): the split-KV forward for few query
+    rows against a long key sequence (same arguments and results as
+    forward, plus the number of key splits, 0 = the library's choice)."""
+    import torch
+
+    validate_attention_inputs(q, k, v)
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    need = int(lib.fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, int(bool(causal)), int(window), int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(window), int(num_splits),
+                           ws_ptr, ws_bytes, _stream_ptr(q.device, stream))
+    _check(lib, "fa_fwd_decode", st)
     return out, lse
 
 

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 ARCH = "gfx950"
 
 
@@ -33,13 +33,13 @@ def hipcc() -> str:
 # per-source device flags
 EXTRA = {
     # forward: matrix-core accumulators in VGPRs, so the scores feed the
-    # softmax and O is rescaled without AGPR <-> VGPR copies
     # softmax and O is rescaled without AGPR <-> VGPR copies.  No step of the
     # kernels relies on NaN semantics (scores are finite or -inf), and without
     # them a max needs no extra canonicalising instruction per operand.
     "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-    # backward: likewise
+    # backward and split-KV decoding: likewise
     "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "fa_api.hip": [],
 }
 

@@ -49,6 +49,34 @@ bool band_of(int Nq, int Nk, int causal, int window, int& wl, int& wr) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Split-KV decoding.  The packed query tile holds (H / H_kv) N_q rows; above
+// kDecodeMaxRows the general forward kernel runs instead.
+bool decode_packs(int H, int Hkv, int Nq) { return (long long)(H / Hkv) * Nq <= fa::kDecodeMaxRows; }
+
+// Key stages of 128 that hold a key some query row sees.
+int decode_stages(int Nq, int Nk, int wl, int wr, bool band, bool win) {
+  const int hi_off = Nk - Nq + wr, lo_off = Nk - Nq - wl;
+  const int klast = band ? (Nk - 1 < Nq - 1 + hi_off ? Nk - 1 : Nq - 1 + hi_off) : Nk - 1;
+  const int kfirst = win ? (lo_off > 0 ? lo_off : 0) : 0;
+  if (klast < kfirst) return 0;
+  return klast / fa::kDecodeStageKeys - kfirst / fa::kDecodeStageKeys + 1;
+}
+
+// Splits per (batch, key head): the caller's number if given.  Otherwise
+// one round of workgroups on a 256-CU MI355X (the d = 128 kernel holds
+// 128 KiB of LDS, one workgroup per CU; d = 64 half that, two per CU), but
+// at least 4 stages of keys per split, since a short split spends most of
+// its time waiting for its first stage.  Never more splits than stages.
+int decode_splits(int B, int Hkv, int d, int nst, int requested) {
+  const long long units = (long long)B * Hkv;
+  const long long slots = d == 128 ? 256 : 512;
+  long long want = requested > 0 ? requested : (slots + units - 1) / units;
+  if (requested <= 0 && want > nst / 4) want = nst / 4;
+  if (want > nst) want = nst;
+  if (want > 256) want = 256;
+  return want < 1 ? 1 : (int)want;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +92,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_SCALE: return "scale must be a finite float";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "causal must be 0 or 1, window must not be negative, and outputs must not overlap inputs";
+    case FA_ERR_ARG: return "causal must be 0 or 1, window and num_splits must not be negative, and outputs must not overlap inputs";
   }
   return "unknown status";
 }
@@ -107,6 +135,68 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);
   a.negate = scale < 0.f;
   const hipError_t e = fa::launch_fwd(a, d, band, window > 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int window,
+                                 int num_splits) {
+  if (check_shape(B, H, Hkv, Nq, Nk, d) != FA_OK || causal < 0 || causal > 1 || window < 0 || num_splits < 0)
+    return 0;
+  if (!decode_packs(H, Hkv, Nq)) return 0;
+  int wl, wr;
+  const bool band = band_of(Nq, Nk, causal, window, wl, wr);
+  const int ns = decode_splits(B, Hkv, d, decode_stages(Nq, Nk, wl, wr, band, window > 0), num_splits);
+  if (ns == 1) return 0;
+  return round256((size_t)ns * B * H * Nq * (d + 1) * sizeof(float));
+}
+
+fa_status fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                        int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((causal != 0 && causal != 1) || window < 0 || num_splits < 0) return FA_ERR_ARG;
+  const size_t need = fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, causal, window, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return FA_ERR_WORKSPACE;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * Hkv * d * 2, lb = (size_t)B * H * Nq * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t insz[3] = {qb, kb, kb};
+  void* outs[3] = {o, lse, workspace};
+  const size_t outsz[3] = {qb, lb, need};
+  for (int i = 0; i < 3; ++i) {
+    if (outsz[i] == 0) continue;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (outsz[j] && overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+  if (!decode_packs(H, Hkv, Nq))  // too many rows per key head to pack: the general forward
+    return fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, stream);
+
+  fa::DecArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.G = H / Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  const bool band = band_of(Nq, Nk, causal, window, a.wl, a.wr);
+  a.nsplit = decode_splits(B, Hkv, d, decode_stages(Nq, Nk, a.wl, a.wr, band, window > 0), num_splits);
+  const size_t rows = (size_t)B * H * Nq;
+  a.part = a.nsplit > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = a.nsplit > 1 ? static_cast<float*>(workspace) + (size_t)a.nsplit * rows * d : nullptr;
+  a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);  // as in the forward
+  a.negate = scale < 0.f;
+  const hipError_t e = fa::launch_decode(a, d, band, window > 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_bwd", "fa_bwd_qk", "fa_bwd_ex",
-         "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
+        ["fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_fwd_decode", "fa_decode_workspace_size", "fa_bwd",
+         "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -173,6 +173,57 @@ def test_grouped_heads_and_window_validation(lib):
     assert fwd_ex(lib, H=4, Hkv=1, o=P[1] + 16384 - 256) == -9
     assert fwd_ex(lib, H=4, Hkv=1, o=P[1] + 16384, scale=nan) == -7
     assert bwd_ex(lib, H=4, Hkv=1, dk=P[2] + 16384 - 256) == -9
+
+
+def dec(lib, H=8, Hkv=2, Nq=1, Nk=4096, d=128, B=1, scale=0.125, causal=1, window=0, splits=0, ws=P[9],
+        ws_bytes=None, **ptrs):
+    p = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4])
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, causal, window, splits)
+    return lib.fa_fwd_decode(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, Hkv, Nq, Nk, d, scale, causal,
+                             window, splits, ws, ws_bytes, None)
+
+
+def test_decode_workspace_size(lib):
+    r256 = lambda x: (x + 255) // 256 * 256
+    size = lib.fa_decode_workspace_size
+    # 8 query heads over 2 key heads, one position, 4096 keys = 32 stages of
+    # 128: 2 units of (batch, key head) would take 128 splits to fill 256
+    # CUs, capped at 32 / 4 = 8 so each split keeps 4 stages
+    assert size(1, 8, 2, 1, 4096, 128, 1, 0, 0) == r256(8 * 8 * 1 * 129 * 4)
+    assert size(1, 8, 2, 1, 65536, 128, 1, 0, 0) == r256(128 * 8 * 129 * 4)   # 512 stages: 128 splits
+    assert size(1, 8, 2, 1, 65536, 64, 1, 0, 0) == r256(128 * 8 * 65 * 4)     # d = 64: 256 -> capped 128
+    assert size(4, 8, 8, 1, 65536, 128, 1, 0, 0) == r256(8 * 32 * 129 * 4)    # 32 units: 8 splits
+    assert size(1, 8, 2, 1, 4096, 128, 1, 0, 5) == r256(5 * 8 * 129 * 4)      # as asked
+    assert size(1, 8, 2, 1, 4096, 128, 1, 0, 99) == r256(32 * 8 * 129 * 4)    # at most one per stage
+    assert size(1, 8, 2, 1, 4096, 128, 1, 0, 1) == 0              # one split: no partials
+    assert size(1, 8, 2, 1, 100, 64, 1, 0, 0) == 0                # one stage of keys
+    assert size(300, 8, 1, 1, 4096, 128, 1, 0, 0) == 0            # 300 units fill the GPU
+    # a window of 256 keys at the end of 65536: keys 65280 .. 65535, 2 stages
+    assert size(1, 8, 2, 1, 65536, 128, 1, 256, 2) == r256(2 * 8 * 129 * 4)
+    assert size(1, 8, 2, 1, 65536, 128, 1, 256, 3) == r256(2 * 8 * 129 * 4)
+    assert size(1, 8, 2, 1, 65536, 128, 1, 257, 3) == r256(3 * 8 * 129 * 4)  # one key more: 3 stages
+    assert size(1, 64, 1, 1, 4096, 128, 1, 0, 0) == 0             # 64 rows per key head: not packed
+    assert size(1, 8, 2, 1, 4096, 128, 1, 0, -1) == 0             # invalid
+    assert size(1, 6, 4, 1, 4096, 128, 1, 0, 0) == 0              # invalid
+
+
+def test_decode_validation(lib):
+    nan = float("nan")
+    assert dec(lib, q=None) == -1
+    assert dec(lib, Hkv=3) == -2
+    assert dec(lib, d=96) == -3
+    assert dec(lib, o=P[3] + 8) == -5
+    assert dec(lib, scale=nan) == -7
+    assert dec(lib, splits=-1) == -9
+    assert dec(lib, window=-1) == -9
+    assert dec(lib, ws=None) == -6                                   # 32 splits need a workspace
+    assert dec(lib, ws_bytes=100) == -6
+    assert dec(lib, ws=P[9] + 64) == -6
+    assert dec(lib, o=P[1]) == -9                                    # output aliases K
+    assert dec(lib, ws=P[2]) == -9                                   # workspace aliases V
+    assert dec(lib, splits=1, ws=None, ws_bytes=0, scale=nan) == -7   # one split needs no workspace
 
 
 def test_workspace_size(lib):
