@@ -40,6 +40,10 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+#ifndef FWD_KAHEAD
+#define FWD_KAHEAD 4  // score-product K operands requested ahead of their use
+#endif
+
 namespace fa {
 
 // BAND: the visible keys have an upper edge (causal, or a window); WIN: they
@@ -194,23 +198,37 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   float l_run = 0.f;                // this lane's half of the running sum
   const float c = a.c;
 
-  // Work on one key tile held in LDS.  MASK (std::true_type or
-  // std::false_type) selects the variant for tiles crossing this wave's
-  // diagonal; every other tile runs without a single masking instruction.
-  auto compute_tile = [&](auto MASK, int kb, const lds_char* kt_lds, const lds_char* vt_lds) __attribute__((always_inline)) {
+  // Work on one key tile held in LDS: the scores and their softmax (into
+  // bf16 probabilities pk, moving the running maximum and rescaling O and l
+  // when it grows), then O += P V.  MASK (std::true_type or
+  // std::false_type) selects the variant for tiles crossing a band edge of
+  // this wave's rows; every other tile runs without a masking instruction.
+  auto scores_softmax = [&](auto MASK, int kb, const lds_char* kt_lds, uint32_t (&pk)[NSB][8])
+      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
-    // S^T (keys x queries) for each 32-key sub-block.  All K operands of a
-    // sub-block are requested from LDS before its first product so the
-    // reads overlap the matrix-core work instead of each product waiting.
+    // S^T (keys x queries) for each 32-key sub-block: NSB * NKK products in
+    // one stream, the K operand of product j + KA requested from LDS when
+    // product j issues (a ring of KA + 1 operands).  The scheduling barriers
+    // keep the compiler from pulling the reads back to their use, which
+    // would make each product wait out a full LDS latency.
     f32x16 sacc[NSB];
+    {
+      constexpr int NJ = NSB * NKK;
+      bf16x8 ring[FWD_KAHEAD + 1];
+      auto read_k = [&](int j) __attribute__((always_inline)) {
+        ring[j % (FWD_KAHEAD + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff[j % NKK]);
+      };
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      bf16x8 kop[NKK];
+      for (int j = 0; j < FWD_KAHEAD && j < NJ; ++j) read_k(j);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kop[kk] = lds_read16(kt_lds + sb * 32 * ROWB + koff[kk]);
-      sacc[sb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sacc[sb] = mfma32(kop[kk], qop[kk], sacc[sb]);
+      for (int j = 0; j < NJ; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + FWD_KAHEAD < NJ) read_k(j + FWD_KAHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+        const int sb = j / NKK, kk = j % NKK;
+        sacc[sb] = mfma32(ring[j % (FWD_KAHEAD + 1)], qop[kk], kk == 0 ? f32x16{} : sacc[sb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // mask on tiles crossing a band edge: invisible key -> -inf.  The scale
@@ -254,7 +272,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     // tile can leave a row without a key so far (m = -inf, every p = 0); after
     // an unmasked tile m is finite.
     const float negm = (MASKED && m_run == -__builtin_inff()) ? 0.f : -m_run;
-    uint32_t pk[NSB][8];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -264,9 +281,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
         l_run += p0 + p1;
         pk[sb][e >> 1] = pack_bf16x2(p0, p1);
       }
-
-    // O^T += V^T P^T over the tile's keys, 16 at a time; the V^T operands of
-    // one key step are all requested before its products
+  };
+  // O^T += V^T P^T over the tile's keys, 16 at a time; the V^T operands of
+  // one key step are all requested before its products
+  auto pv_product = [&](const uint32_t (&pk)[NSB][8], const lds_char* vt_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int sb = t >> 1, hf = t & 1;
@@ -282,6 +300,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(vop[db], pop, oacc[db]);
     }
+  };
+  auto compute_tile = [&](auto MASK, int kb, const lds_char* kt_lds, const lds_char* vt_lds) __attribute__((always_inline)) {
+    uint32_t pk[NSB][8];
+    scores_softmax(MASK, kb, kt_lds, pk);
+    pv_product(pk, vt_lds);
   };
 
   // one key tile: wait for its copies, start the next tile's copies into
