@@ -40,28 +40,24 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
-#ifndef FWD_KAHEAD
-#define FWD_KAHEAD 4  // score-product K operands requested ahead of their use
-#endif
 
 namespace fa {
 
 // BAND: the visible keys have an upper edge (causal, or a window); WIN: they
 // also have a lower edge (a window).  Without BAND every key is visible.
 template <int D, int NW, int BC, bool BAND, bool WIN>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel(FwdArgs a) {
   static_assert(BAND || !WIN, "a window always bounds the keys above");
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
   constexpr int TILEB = BC * ROWB;       // bytes of one K or V tile
   constexpr int NCH = D / 8;             // 16-byte chunks per row
   constexpr int LOADS = TILEB / 1024;    // 1 KiB wave copies per tile
-  constexpr int LPW = LOADS / NW;        // copies per wave per tile
+  constexpr int LPW = (LOADS + NW - 1) / NW;  // copies per wave per tile (the last may be idle)
   constexpr int NSB = BC / 32;           // 32-key sub-blocks of a tile
   constexpr int NDB = D / 32;            // 32-wide column blocks of O
   constexpr int NKK = D / 16;            // k-steps of the score product
   constexpr int NT = BC / 16;            // k-steps of the PV product
-  static_assert(LOADS % NW == 0, "tile copies must split evenly over waves");
 
   // Four separate LDS objects (K and V, two buffers each) and a loop unrolled
   // by two: every access names its buffer at compile time, so the compiler
@@ -156,14 +152,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   }
   // direct HBM -> LDS copies: wave copy c = w + NW i fills LDS bytes
   // [1024 c, 1024 c + 1024) of a tile; lane l fills 16-byte slot 64 c + l,
-  // i.e. tile row p / NCH, swizzled chunk p % NCH.
-  // (byte offsets from the tile's first row, one unsigned 32-bit value per copy)
-  uint32_t goff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int p = 64 * (w + NW * i) + l;
+  // i.e. tile row p / NCH, swizzled chunk p % NCH.  Copy i of a wave reads
+  // RSTEP i rows further down than its copy 0, and RSTEP is a multiple of 16,
+  // where the swizzle repeats, so one per-lane byte offset (from the tile's
+  // first row) serves every copy, the rest going into the scalar offset.
+  constexpr int RSTEP = 64 * NW / NCH;
+  static_assert(RSTEP % 16 == 0, "copies of a wave must keep the row swizzle");
+  uint32_t goff;
+  {
+    const int p = 64 * w + l;
     const int row = p / NCH, ch = p % NCH;
-    goff[i] = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    goff = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
   }
   // K and V of this (batch, key head) as buffer resources: rows 0 .. N_k - 1
   // at a stride of H_kv d elements, the last ending H_kv d - hk d elements
@@ -177,8 +176,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds_buf(krs, goff[i], soff, (lds_void*)(kdst + c * 1024));
-      copy16_to_lds_buf(vrs, goff[i], soff, (lds_void*)(vdst + c * 1024));
+      if (LOADS % NW != 0 && c >= LOADS) break;  // (wave-uniform)
+      const uint32_t so = soff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
+      copy16_to_lds_buf(krs, goff, so, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(vrs, goff, so, (lds_void*)(vdst + c * 1024));
     }
   };
 
@@ -210,23 +211,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     // one stream, the K operand of product j + KA requested from LDS when
     // product j issues (a ring of KA + 1 operands).  The scheduling barriers
     // keep the compiler from pulling the reads back to their use, which
-    // would make each product wait out a full LDS latency.
+    // would make each product wait out a full LDS latency.  With three
+    // waves per SIMD the other waves cover most of that latency, and the
+    // registers of a deeper ring are not there (KA = 1); with two, KA = 4.
+    constexpr int KA = NW >= 12 ? 1 : 4;
     f32x16 sacc[NSB];
     {
       constexpr int NJ = NSB * NKK;
-      bf16x8 ring[FWD_KAHEAD + 1];
+      bf16x8 ring[KA + 1];
       auto read_k = [&](int j) __attribute__((always_inline)) {
-        ring[j % (FWD_KAHEAD + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff[j % NKK]);
+        ring[j % (KA + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff[j % NKK]);
       };
 #pragma unroll
-      for (int j = 0; j < FWD_KAHEAD && j < NJ; ++j) read_k(j);
+      for (int j = 0; j < KA && j < NJ; ++j) read_k(j);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         __builtin_amdgcn_sched_barrier(0);
-        if (j + FWD_KAHEAD < NJ) read_k(j + FWD_KAHEAD);
+        if (j + KA < NJ) read_k(j + KA);
         __builtin_amdgcn_sched_barrier(0);
         const int sb = j / NKK, kk = j % NKK;
-        sacc[sb] = mfma32(ring[j % (FWD_KAHEAD + 1)], qop[kk], kk == 0 ? f32x16{} : sacc[sb]);
+        sacc[sb] = mfma32(ring[j % (KA + 1)], qop[kk], kk == 0 ? f32x16{} : sacc[sb]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -381,14 +385,22 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, BAND, WIN>, grid, block, args, 0, stream);
 }
 
-template <int D, int NW, int BC>
-static hipError_t launch_fwd_d(const FwdArgs& a, bool band, bool win, hipStream_t stream) {
-  if (win) return launch_fwd_t<D, NW, BC, true, true>(a, stream);
-  return band ? launch_fwd_t<D, NW, BC, true, false>(a, stream) : launch_fwd_t<D, NW, BC, false, false>(a, stream);
-}
-
+// d = 128: the causal kernel fits in 168 registers, so one 12-wave
+// workgroup (384 query rows) runs three waves per SIMD.  That halves the
+// workgroup count of a short sequence, so it is used only where at least
+// 1024 workgroups remain (four per CU); otherwise, and for the full and
+// windowed kernels (which need more registers), 8 waves of 256 rows run two
+// per SIMD.  d = 64: 4 waves (128 rows).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
-  return d == 128 ? launch_fwd_d<128, 8, 64>(a, band, win, stream) : launch_fwd_d<64, 4, 64>(a, band, win, stream);
+  if (d == 128) {
+    if (win) return launch_fwd_t<128, 8, 64, true, true>(a, stream);
+    if (!band) return launch_fwd_t<128, 8, 64, false, false>(a, stream);
+    const long wgs12 = (long)a.B * a.H * ((a.Nq + 383) / 384);
+    return wgs12 >= 1024 ? launch_fwd_t<128, 12, 64, true, false>(a, stream)
+                         : launch_fwd_t<128, 8, 64, true, false>(a, stream);
+  }
+  if (win) return launch_fwd_t<64, 4, 64, true, true>(a, stream);
+  return band ? launch_fwd_t<64, 4, 64, true, false>(a, stream) : launch_fwd_t<64, 4, 64, false, false>(a, stream);
 }
 
 }  // namespace fa
