@@ -348,11 +348,12 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
     tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
     if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
   }
-  if (nloop < ntiles) {  // the ragged last tile of an unbanded walk
-    if (nloop & 1)
-      tile_step(std::true_type{}, nloop, K1, V1, K0, V0);
-    else
-      tile_step(std::true_type{}, nloop, K0, V0, K1, V1);
+  if (nloop < ntiles) {
+    // the ragged last tile of an unbanded walk, from whichever buffer holds
+    // it (picked at run time: no copy is in flight any more, so the
+    // compiler has nothing to hold the reads back for)
+    const bool odd = nloop & 1;
+    tile_step(std::true_type{}, nloop, odd ? K1 : K0, odd ? V1 : V0, odd ? K0 : K1, odd ? V0 : V1);
   }
 
   if (!wave_active) return;
