@@ -14,8 +14,9 @@
 //  * one workgroup = NW wave64s, each wave owning 32 query rows (Br = 32 NW);
 //    the query tile lives in VGPRs for the whole kernel;
 //  * K and V tiles of BC keys stream through LDS, double buffered, copied
-//    straight from HBM into LDS (global_load_lds, no VGPR staging) with an
-//    XOR chunk swizzle so the matrix-core operand reads are conflict free;
+//    straight from HBM into LDS (global_load_lds, no VGPR staging) in the
+//    row-group layout (fa_device.h) so the matrix-core operand reads are
+//    conflict free and each transpose read takes 128 contiguous bytes;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    so every lane holds 32 scores of ONE query row: the row max needs one
 //    cross-half exchange, the row sum none until the end, and the rescale
@@ -125,44 +126,36 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
     for (int kk = 0; kk < NKK; ++kk) qop[kk] = bf16x8{};
   }
 
-  // ---- per-lane LDS read offsets
-  // K operand of S^T = K Q^T: row 32 s + l32, chunk 2 kk + h2.
-  int koff[NKK];
-  {
-    const int sw = chunk_swizzle<D>(l32);
+  // ---- per-lane LDS read offsets (K and V tiles in the row-group layout)
+  // K operand of S^T = K Q^T: row 32 s + l32, piece 2 kk + h2, at
+  // krb[kk & 1] + 256 (kk / 2) + s 32 ROWB
+  int krb[2];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + h2) ^ sw) << 4);
-  }
+  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  auto koff = [&](int kk) __attribute__((always_inline)) { return krb[kk & 1] + 256 * (kk >> 1); };
   // V^T operand by transpose reads: group g = l / 16, lane j = l % 16 reads
   // row 16 t + 4 h2 + j / 4 (+ 8 for the second read), columns
-  // 32 dblk + 16 (g % 2) + 4 (j % 4) .. +3.
-  int voff[2][NDB];
+  // 32 db + 16 (g % 2) + 4 (j % 4) .. +3, at vrb[r] + 256 db + 16 t ROWB
+  int vrb[2];
   {
     const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 4 * h2 + (j >> 2) + 8 * r;
-      const int sw = chunk_swizzle<D>(row);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int ch = 4 * db + 2 * (g & 1) + ((j & 3) >> 1);
-        voff[r][db] = row * ROWB + ((ch ^ sw) << 4) + 8 * (j & 1);
-      }
-    }
+    for (int r = 0; r < 2; ++r)
+      vrb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
   }
   // direct HBM -> LDS copies: wave copy c = w + NW i fills LDS bytes
   // [1024 c, 1024 c + 1024) of a tile; lane l fills 16-byte slot 64 c + l,
-  // i.e. tile row p / NCH, swizzled chunk p % NCH.  Copy i of a wave reads
-  // RSTEP i rows further down than its copy 0, and RSTEP is a multiple of 16,
-  // where the swizzle repeats, so one per-lane byte offset (from the tile's
-  // first row) serves every copy, the rest going into the scalar offset.
+  // which holds the piece rg_slot names.  Copy i of a wave reads RSTEP i
+  // rows further down than its copy 0, and RSTEP is a multiple of 16, where
+  // the layout repeats, so one per-lane byte offset (from the tile's first
+  // row) serves every copy, the rest going into the scalar offset.
   constexpr int RSTEP = 64 * NW / NCH;
-  static_assert(RSTEP % 16 == 0, "copies of a wave must keep the row swizzle");
+  static_assert(RSTEP % 16 == 0, "copies of a wave must keep the row-group layout");
   uint32_t goff;
   {
-    const int p = 64 * w + l;
-    const int row = p / NCH, ch = p % NCH;
-    goff = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    int row, piece;
+    rg_slot<D>(64 * w + l, row, piece);
+    goff = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
   // K and V of this (batch, key head) as buffer resources: rows 0 .. N_k - 1
   // at a stride of H_kv d elements, the last ending H_kv d - hk d elements
@@ -220,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
       constexpr int NJ = NSB * NKK;
       bf16x8 ring[KA + 1];
       auto read_k = [&](int j) __attribute__((always_inline)) {
-        ring[j % (KA + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff[j % NKK]);
+        ring[j % (KA + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff(j % NKK));
       };
 #pragma unroll
       for (int j = 0; j < KA && j < NJ; ++j) read_k(j);
@@ -297,8 +290,8 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
       bf16x8 vop[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x4 v0 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[0][db]);
-        const bf16x4 v1 = lds_read_tr16(vt_lds + 16 * t * ROWB + voff[1][db]);
+        const bf16x4 v0 = lds_read_tr16(vt_lds + 16 * t * ROWB + 256 * db + vrb[0]);
+        const bf16x4 v1 = lds_read_tr16(vt_lds + 16 * t * ROWB + 256 * db + vrb[1]);
         vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
