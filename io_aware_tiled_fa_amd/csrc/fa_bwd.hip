@@ -35,6 +35,9 @@
 #ifndef PROD_AHEAD
 #define PROD_AHEAD 3
 #endif
+#ifndef DQ_PIPE
+#define DQ_PIPE 1  // dQ kernel: sub-blocks software-pipelined (dS beside products)
+#endif
 #ifndef CONS_AHEAD
 #define CONS_AHEAD 2
 #endif
@@ -177,22 +180,22 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   const size_t qb_off = (size_t)b * a.Nq * rs;                   // Q, dO of batch b
   const size_t kv_off = (size_t)b * a.Nk * rk + (size_t)hk * D;  // K, V, dK, dV
 
-  // ---- per-lane LDS offsets.  Q / dO tiles use the forward kernel's
-  // geometry; the swizzle XORs the chunk index, so a power-of-two chunk step
-  // is an XOR of the offset.
-  // producer row reads (A operand, lane = row l32, chunk 2 kk + h2) at roff ^ (kk << 5)
-  const int roff = l32 * ROWB + ((chunk_swizzle<D>(l32) ^ h2) << 4);
-  // consumer transpose reads: rows 4 h2 + j/4 (+8) of a 16-row step, columns
-  // 32 db + 16 (g&1) + 4 (j&3), at troff0[r] ^ (db << 6)
-  int troff0[2];
+  // ---- per-lane LDS offsets.  Q / dO tiles are in the row-group layout
+  // (fa_device.h), read as rows by the producers and by transpose reads by
+  // the consumers.
+  // producer row reads (A operand, lane = row l32, piece 2 kk + h2) at
+  // krb[kk & 1] + 256 (kk / 2)
+  int krb[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  // consumer transpose reads: rows 4 h2 + j/4 (+8 r) of a 16-row step, columns
+  // 32 db + 16 (g&1) + 4 (j&3), at trb[r] + 256 db
+  int trb[2];
   {
     const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 4 * h2 + (j >> 2) + 8 * r;
-      const int ch = 2 * (g & 1) + ((j & 3) >> 1);
-      troff0[r] = row * ROWB + ((ch ^ chunk_swizzle<D>(row)) << 4) + 8 * (j & 1);
-    }
+    for (int r = 0; r < 2; ++r)
+      trb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
   }
   // P^T / dS^T chunk of this lane: key row 32 kg + l32, queries 8 g4 + 4 h2 at
   // pbase ^ (16 g4)
@@ -207,9 +210,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < QLPW; ++i) {
     const int c = ((w & 3) + 4 * i) % (QTILEB / 1024);
-    const int p = 64 * c + l;
-    const int row = p / NCH, ch = p % NCH;
-    qgoff[i] = (uint32_t)(row * (int)rs + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    int row, piece;
+    rg_slot<D>(64 * c + l, row, piece);
+    qgoff[i] = (uint32_t)(row * (int)rs + piece * 8) * 2u;
   }
   // buffer I (a std::integral_constant) of each kind
   auto QT = [&](auto I) __attribute__((always_inline)) {
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
       constexpr int PD = PROD_AHEAD;  // k-steps the operand reads run ahead
       bf16x8 ring[PD + 1][2];
       auto read_rows = [&](int kk, bf16x8 (&dst2)[2]) __attribute__((always_inline)) {
-        const int off = roff ^ (kk << 5);
+        const int off = krb[kk & 1] + 256 * (kk >> 1);
         dst2[0] = lds_read16(qt + off);
         dst2[1] = lds_read16(gt + off);
       };
@@ -453,8 +456,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
         pa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
         sa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
       }
-      const int o0 = 16 * tq * ROWB + (troff0[0] ^ (db << 6));
-      const int o1 = 16 * tq * ROWB + (troff0[1] ^ (db << 6));
+      const int o0 = 16 * tq * ROWB + 256 * db + trb[0];
+      const int o1 = 16 * tq * ROWB + 256 * db + trb[1];
       go[s] = __builtin_shufflevector(lds_read_tr16(gt + o0), lds_read_tr16(gt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
       qo[s] = __builtin_shufflevector(lds_read_tr16(qt + o0), lds_read_tr16(qt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
     };
@@ -581,28 +584,29 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk) qop[kk] = gop[kk] = bf16x8{};
   }
 
-  // ---- per-lane LDS offsets (the forward kernel's geometry)
-  // K / V rows as A operands: row 32 sb + l32, chunk 2 kk + h2
-  const int roff = l32 * ROWB + ((chunk_swizzle<D>(l32) ^ h2) << 4);
-  // K^T by transpose reads: rows 16 t + 4 h2 + j/4 (+8), columns 32 db + 16 (g&1) + 4 (j&3)
-  int troff0[2];
+  // ---- per-lane LDS offsets (K and V tiles in the row-group layout)
+  // K / V rows as A operands: row 32 sb + l32, piece 2 kk + h2, at
+  // krb[kk & 1] + 256 (kk / 2) + sb 32 ROWB
+  int krb[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  // K^T by transpose reads: rows 16 t + 4 h2 + j/4 (+8 r), columns
+  // 32 db + 16 (g&1) + 4 (j&3), at trb[r] + 256 db + 16 t ROWB
+  int trb[2];
   {
     const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 4 * h2 + (j >> 2) + 8 * r;
-      const int ch = 2 * (g & 1) + ((j & 3) >> 1);
-      troff0[r] = row * ROWB + ((ch ^ chunk_swizzle<D>(row)) << 4) + 8 * (j & 1);
-    }
+    for (int r = 0; r < 2; ++r)
+      trb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
   }
   // (byte offsets, one unsigned 32-bit value per copy, into buffer resources
   // over this head's K and V rows, sized as in the forward kernel)
   uint32_t goff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int p = 64 * (w + NW * i) + l;
-    const int row = p / NCH, ch = p % NCH;
-    goff[i] = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+    int row, piece;
+    rg_slot<D>(64 * (w + NW * i) + l, row, piece);
+    goff[i] = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
   const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);  // (rows past N_k read zero)
   const buf_rsrc krs = make_rsrc(kbase, head_bytes);
@@ -630,6 +634,100 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
 
+#if DQ_PIPE
+  // One key tile as two 32-key sub-blocks, software-pipelined so the dS
+  // work (VALU) of one sub-block runs beside independent matrix-core
+  // products of the same wave:
+  //   S^T, dP^T of sub-block 0
+  //   S^T, dP^T of sub-block 1      beside  dS^T of sub-block 0
+  //   dQ^T += K0^T dS0^T            beside  dS^T of sub-block 1
+  //   dQ^T += K1^T dS1^T
+  // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e), masked outside the
+  // row's band; one element pair per product, pinned there by an empty asm.
+  static_assert(NSB == 2, "the pipelined tile needs 64-key tiles");
+  auto compute_tile = [&](auto MASK, int kb, const lds_char* __restrict__ kt_lds,
+                          const lds_char* __restrict__ vt_lds) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(MASK)::value;
+    const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;  // last visible key
+    const int lo = qrow + lo_off;                                     // first (banded)
+    auto ds_pair = [&](int sb, int u, const f32x16& sv, const f32x16& pv, uint32_t (&dspk)[8])
+        __attribute__((always_inline)) {
+      const int e = 2 * u;
+      float p0 = fast_exp2(fmaf(sv[e], c, nl));
+      float p1 = fast_exp2(fmaf(sv[e + 1], c, nl));
+      if constexpr (MASKED) {  // key outside the row's band, or key >= N_k
+        const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
+        p0 = (key > hi || (WIN && key < lo)) ? 0.f : p0;
+        p1 = (key + 1 > hi || (WIN && key + 1 < lo)) ? 0.f : p1;
+      }
+      dspk[u] = pack_bf16x2(p0 * (pv[e] + ndr), p1 * (pv[e + 1] + ndr));
+      asm volatile("" : "+v"(dspk[u]));
+    };
+    // S^T and dP^T of sub-block sb (lane: [key 8(e/4)+4h2+e%4][query l32]);
+    // the K / V operands of k-step kk + 2 requested before the products of
+    // kk; with PREV, the dS of sub-block 0 spread over the k-steps
+    auto sdp = [&](int sb, f32x16& sacc, f32x16& pacc, auto PREV, const f32x16& sp, const f32x16& pp,
+                   uint32_t (&dsp)[8]) __attribute__((always_inline)) {
+      sacc = f32x16{};
+      pacc = f32x16{};
+      bf16x8 ring[3][2];
+      auto read_kv = [&](int kk, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+        const int off = sb * 32 * ROWB + krb[kk & 1] + 256 * (kk >> 1);
+        dst[0] = lds_read16(kt_lds + off);
+        dst[1] = lds_read16(vt_lds + off);
+      };
+      read_kv(0, ring[0]);
+      read_kv(1, ring[1]);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 2 < NKK) read_kv(kk + 2, ring[(kk + 2) % 3]);
+        sacc = mfma32(ring[kk % 3][0], qop[kk], sacc);
+        pacc = mfma32(ring[kk % 3][1], gop[kk], pacc);
+        if constexpr (decltype(PREV)::value) {
+#pragma unroll
+          for (int u = kk * 8 / NKK; u < (kk + 1) * 8 / NKK; ++u) ds_pair(sb - 1, u, sp, pp, dsp);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // dQ^T += K^T dS^T over sub-block sb's 32 keys (two steps of 16); with
+    // NEXT, the dS of sub-block 1 spread over the products
+    auto dqmm = [&](int sb, const uint32_t (&dspk)[8], auto NEXT, const f32x16& sn, const f32x16& pn,
+                    uint32_t (&dsn)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        const bf16x8 sop = __builtin_bit_cast(bf16x8, u32x4{dspk[4 * tq], dspk[4 * tq + 1], dspk[4 * tq + 2], dspk[4 * tq + 3]});
+        const int t = 2 * sb + tq;
+        bf16x8 kop[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x4 k0 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[0]);
+          const bf16x4 k1 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[1]);
+          kop[db] = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          __builtin_amdgcn_sched_barrier(0);
+          dqacc[db] = mfma32(kop[db], sop, dqacc[db]);
+          if constexpr (decltype(NEXT)::value) {
+            constexpr int NP = 2 * NDB;  // products of this sub-block
+            const int i = tq * NDB + db;
+#pragma unroll
+            for (int u = i * 8 / NP; u < (i + 1) * 8 / NP; ++u) ds_pair(sb + 1, u, sn, pn, dsn);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    f32x16 s0, p0, s1, p1;
+    uint32_t d0[8], d1[8];
+    sdp(0, s0, p0, std::false_type{}, s0, p0, d0);
+    sdp(1, s1, p1, std::true_type{}, s0, p0, d0);
+    dqmm(0, d0, std::true_type{}, s1, p1, d1);
+    dqmm(1, d1, std::false_type{}, s1, p1, d1);
+  };
+#else
   auto compute_tile = [&](auto MASK, int kb, const lds_char* __restrict__ kt_lds,
                           const lds_char* __restrict__ vt_lds) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
@@ -642,7 +740,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       bf16x8 ring[3][2];
       auto read_kv = [&](int kk, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-        const int off = sb * 32 * ROWB + (roff ^ (kk << 5));
+        const int off = sb * 32 * ROWB + krb[kk & 1] + 256 * (kk >> 1);
         dst[0] = lds_read16(kt_lds + off);
         dst[1] = lds_read16(vt_lds + off);
       };
@@ -678,8 +776,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
         bf16x8 kop[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x4 k0 = lds_read_tr16(kt_lds + 16 * t * ROWB + (troff0[0] ^ (db << 6)));
-          const bf16x4 k1 = lds_read_tr16(kt_lds + 16 * t * ROWB + (troff0[1] ^ (db << 6)));
+          const bf16x4 k0 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[0]);
+          const bf16x4 k1 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[1]);
           kop[db] = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
@@ -688,6 +786,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+
+#endif
 
   // MAYMASK: whether the tile can need masking (tiles crossing a band edge,
   // or the ragged last tile); unbanded loops never instantiate the masked
