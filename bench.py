@@ -40,6 +40,11 @@ PEAK_HBM_GBS = 8000.0
 FWD = dict(name="fwd_b1_h32_n32768_d128_causal", B=1, H=32, N=32768, d=128, causal=True)
 BWD = dict(name="bwd_b4_h16_n4096_d128_causal", B=4, H=16, N=4096, d=128, causal=True)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_b1_h32_n32768_d128_causal_hbm_counters.json")
+PIPE_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_kernels_mfma_lds_counters.md")
+# the forward kernel the long-context batch runs: 12 waves of 32 query rows
+FWD_KERNEL = "fwd_kernel<128, 12, 64, true, false>"
+FWD_KERNEL_DESC = "fwd_kernel<128,12,64,true,false> (12 waves, 384 query rows per workgroup, 64-key tiles)"
+FWD_ROWS_PER_WG, FWD_THREADS_PER_WG = 384, 768
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
 
@@ -96,9 +101,9 @@ def read_traffic():
 
 HBM_COMMANDS = [
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/hbm_fetch -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/hbm_write -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
     "python3 bench.py --hbm-summary gpurun_out/hbm_fetch gpurun_out/hbm_write",
 ]
 
@@ -111,14 +116,14 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     import csv
     import glob
 
-    fwd_threads = FWD["B"] * FWD["H"] * (FWD["N"] // 256) * 512
+    fwd_threads = FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG
 
     def read(d, counter):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
         fwd = [float(r["Counter_Value"]) for r in rows
-               if "fwd_kernel<128" in r["Kernel_Name"] and int(r["Grid_Size"]) == fwd_threads]
+               if FWD_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == fwd_threads]
         copy = [float(r["Counter_Value"]) for r in rows if "fa::" not in r["Kernel_Name"]
                 and float(r["Counter_Value"]) > 2 ** 18]  # the 1 GiB copies (KiB units)
         if not fwd or not copy:
@@ -131,7 +136,7 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
     rd, wr = f_kib * f_scale * 1024, w_kib * w_scale * 1024
     return {
-        "kernel": "fwd_kernel<128,8,64,true>",
+        "kernel": FWD_KERNEL_DESC,
         "workload": FWD["name"],
         "kernel_source_hash": kernel_source_hash(),
         "fetch_kib_per_launch_raw": round(f_kib, 1),
@@ -147,6 +152,98 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
         "launches": {"fetch": nf, "write": nw, "copy_fetch": ncf, "copy_write": ncw},
         "commands": HBM_COMMANDS,
     }
+
+
+# Pipe-utilisation counters of the kernels of one step: two rocprofv3 passes
+# (a pass holds at most 8 SQ counters), then a summary into PIPE_FILE.
+PIPE_PASSES = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
+    "GRBM_GUI_ACTIVE",
+]
+PIPE_COMMANDS = [
+    f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pipe{i} -o p -- "
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next" for i, c in enumerate(PIPE_PASSES)
+] + ["python3 bench.py --pipe-summary gpurun_out/pipe0 gpurun_out/pipe1"]
+
+
+def pipe_summary(dirs) -> str:
+    """Per kernel of the step (last dispatch of each): matrix-core busy and
+    co-execution as a share of the cycles of all SIMDs, VALU and LDS issue
+    as a share of wave cycles, LDS busy and bank-conflict cycles per CU."""
+    import collections
+    import csv
+    import glob
+
+    per = collections.defaultdict(dict)
+    for d in dirs:
+        last = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = r["Kernel_Name"].split("(")[0]
+                if "fa::" not in k:
+                    continue
+                key = (k, int(r["Grid_Size"]))
+                did = int(r["Dispatch_Id"])
+                if last.get(key, -1) < did:
+                    last[key] = did
+                    per[key] = {kk: v for kk, v in per[key].items() if not kk.startswith(d + ":")}
+                if did == last[key]:
+                    per[key][d + ":" + r["Counter_Name"]] = per[key].get(d + ":" + r["Counter_Name"], 0.0) + \
+                        float(r["Counter_Value"])
+    lines = ["| kernel | grid threads | cycles (per XCD) | MFMA busy | MFMA+VALU co-exec | VALU issue / wave | "
+             "LDS issue / wave | wait / wave | LDS busy / CU | LDS bank-conflict cycles / LDS busy |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, grid), v in sorted(per.items()):
+        c = {kk.split(":", 1)[1]: x for kk, x in v.items()}
+        if "SQ_WAVE_CYCLES" not in c or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+            continue
+        g = c["GRBM_GUI_ACTIVE"] / 8  # per XCD
+        simd = g * 1024               # 256 CUs x 4 SIMDs over 8 XCDs
+        wc = c["SQ_WAVE_CYCLES"]
+        lines.append(
+            f"| `{k}` | {grid} | {g:.3g} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.1%} | "
+            f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd:.1%} | {c['SQ_ACTIVE_INST_VALU'] / wc:.1%} | "
+            f"{c['SQ_ACTIVE_INST_LDS'] / wc:.1%} | {c['SQ_WAIT_INST_ANY'] / wc:.1%} | "
+            f"{c['SQ_LDS_IDX_ACTIVE'] / (g * 256):.1%} | "
+            f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%} |")
+    return "\n".join(lines)
+
+
+STATS_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_bench_kernel_stats.md")
+STATS_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_stats -o run -- "
+    "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-next",
+    "python3 bench.py --stats-summary gpurun_out/prof_stats",
+]
+
+
+def stats_summary(d: str) -> str:
+    """rocprofv3 --kernel-trace --stats of STATS_COMMANDS as a markdown table:
+    the --stats rows, then each launch shape from the trace."""
+    import collections
+    import csv
+    import glob
+
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0])))
+    trace = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0])))
+    per = collections.defaultdict(list)
+    for r in trace:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), r["Workgroup_Size_X"],
+               r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")), r["LDS_Block_Size"])
+        per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    out = ["## --stats (all dispatches of the run)", "", "| kernel | calls | avg ms | total ms | % |",
+           "|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    out += ["", "## per launch shape (from the kernel trace)", "",
+            "| kernel | workgroups | threads / WG | VGPRs | LDS bytes | dispatches | avg ms | min ms | max ms |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for (k, wgs, wgsz, vg, lds), v in per.items():
+        out.append(f"| `{k}` | {wgs} | {wgsz} | {vg} | {lds} | {len(v)} | {sum(v) / len(v):.4f} | "
+                   f"{min(v):.4f} | {max(v):.4f} |")
+    return "\n".join(out)
 
 
 def device_tensor(bits, device):
@@ -215,9 +312,39 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--stats-summary", metavar="DIR",
+                    help="summarise the STATS_COMMANDS kernel trace into " + os.path.relpath(STATS_FILE, ROOT))
+    ap.add_argument("--pipe-summary", nargs=2, metavar=("PASS0_DIR", "PASS1_DIR"),
+                    help="summarise the PIPE_COMMANDS counter passes into " + os.path.relpath(PIPE_FILE, ROOT))
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the forward kernel's HBM counter summary from two rocprofv3 runs")
     args = ap.parse_args(argv)
+
+    if args.stats_summary:
+        table = stats_summary(args.stats_summary)
+        with open(STATS_FILE, "w") as f:
+            f.write("# rocprofv3 kernel summary\n\n"
+                    "Workloads: fa_fwd on B=1 H=32 N=32768 d=128 causal (the fwd_kernel launch of 2752 "
+                    "workgroups of 768 threads; the smaller fwd_kernel launch is the setup forward of the "
+                    "backward batch) and fa_bwd on B=4 H=16 N=4096 d=128 causal (bwd_pre_kernel, "
+                    "bwd_main_kernel = dK/dV, bwd_dq_kernel = dQ).\n\n"
+                    f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root, MI355X, ROCm 7.2):"
+                    "\n\n```\n" + "\n".join(STATS_COMMANDS) + "\n```\n\n" + table + "\n")
+        print(table)
+        return 0
+
+    if args.pipe_summary:
+        table = pipe_summary(args.pipe_summary)
+        with open(PIPE_FILE, "w") as f:
+            f.write("# Pipe utilisation of the step's kernels (rocprofv3 counters)\n\n"
+                    "One step of bench.py (long-context causal forward, then the backward batch), "
+                    "two counter passes, last dispatch of each kernel. Shares of SIMD cycles assume "
+                    "256 CUs x 4 SIMDs in 8 XCDs; the shader clock under load is about 1.75-1.9 GHz, "
+                    "against the 2.4 GHz of the quoted peak.\n\n"
+                    f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root):\n\n```\n"
+                    + "\n".join(PIPE_COMMANDS) + "\n```\n\n" + table + "\n")
+        print(table)
+        return 0
 
     if args.hbm_summary:
         rec = hbm_summary(*args.hbm_summary)
@@ -337,7 +464,7 @@ def main(argv=None):
             "ms_p90": round(pct(bwd_ms, 0.9), 4), "useful_tflop": round(bf / 1e12, 4),
         },
         "roofline": {
-            "kernel": "fwd_kernel<128,8,64,true,false> (8 waves, 256 query rows per workgroup, 64-key tiles)",
+            "kernel": FWD_KERNEL_DESC,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
