@@ -381,19 +381,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   return hipLaunchKernel((const void*)fwd_kernel<D, NW, BC, BAND, WIN>, grid, block, args, 0, stream);
 }
 
-// d = 128: the causal kernel fits in 168 registers, so one 12-wave
-// workgroup (384 query rows) runs three waves per SIMD.  That halves the
-// workgroup count of a short sequence, so it is used only where at least
-// 1024 workgroups remain (four per CU); otherwise, and for the full and
-// windowed kernels (which need more registers), 8 waves of 256 rows run two
-// per SIMD.  d = 64: 4 waves (128 rows).
+// d = 128: the causal and windowed kernels fit in 168 registers, so one
+// 12-wave workgroup (384 query rows) runs three waves per SIMD.  That
+// shrinks the workgroup count of a short sequence by a third, so it is used
+// only where at least 1024 workgroups remain (four per CU); otherwise, and
+// for full attention (whose kernel needs more registers), 8 waves of 256
+// rows run two per SIMD.  d = 64: 4 waves (128 rows).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
   if (d == 128) {
-    if (win) return launch_fwd_t<128, 8, 64, true, true>(a, stream);
     if (!band) return launch_fwd_t<128, 8, 64, false, false>(a, stream);
-    const long wgs12 = (long)a.B * a.H * ((a.Nq + 383) / 384);
-    return wgs12 >= 1024 ? launch_fwd_t<128, 12, 64, true, false>(a, stream)
-                         : launch_fwd_t<128, 8, 64, true, false>(a, stream);
+    const bool big = (long)a.B * a.H * ((a.Nq + 383) / 384) >= 1024;
+    if (win) return big ? launch_fwd_t<128, 12, 64, true, true>(a, stream) : launch_fwd_t<128, 8, 64, true, true>(a, stream);
+    return big ? launch_fwd_t<128, 12, 64, true, false>(a, stream) : launch_fwd_t<128, 8, 64, true, false>(a, stream);
   }
   if (win) return launch_fwd_t<64, 4, 64, true, true>(a, stream);
   return band ? launch_fwd_t<64, 4, 64, true, false>(a, stream) : launch_fwd_t<64, 4, 64, false, false>(a, stream);

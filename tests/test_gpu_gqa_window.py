@@ -113,3 +113,29 @@ def test_gqa_equals_repeated_heads(fa):
         want = rep.float().view(B, N, Hkv, H // Hkv, d).sum(dim=3)
         err = (got.float() - want).abs().max().item()
         assert err <= 3e-2 + 2 ** -7 * want.abs().max().item(), f"{name}: {err}"
+
+
+@pytest.mark.parametrize("causal,window", [(True, 1000), (False, 700)])
+def test_window_large_grid_ragged(fa, causal, window):
+    """d = 128 windowed grids of at least 1024 workgroups of 384 rows run the
+    12-wave forward kernel; N = 6000 ends ragged in its query tiles.  Sampled
+    rows (tile and window edges, the last rows, a random sample) against the
+    oracle; rows are independent, so a sampled row is exact."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from parity import TOL_LSE, TOL_O, compare, sample_rows, to_numpy_f32
+
+    N = 6000
+    announce(f"fwd window large grid B=2 H=32 N={N} d=128 causal={causal} W={window}")
+    inp = _inputs(2, 32, 8, N, N, 128, 9100 + window, False)
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o, lse = fa.forward(q, k, v, causal=causal, window=window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = sample_rows(N, 40, rng, extra=[383, 384, window - 1, window, window + 383, N - 385])
+    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, 1.0 / math.sqrt(128), causal, rows=rows,
+                                              window=window)
+    compare("O", to_numpy_f32(o)[:, rows], o_ref, TOL_O)
+    compare("LSE", lse.cpu().numpy()[:, :, rows], lse_ref, TOL_LSE, ulp_aware=False)
