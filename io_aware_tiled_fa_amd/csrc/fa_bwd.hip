@@ -114,7 +114,6 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;          // bytes per row of a Q / dO tile
   constexpr int QTILEB = BR * ROWB;    // Q or dO tile
   constexpr int PTB = BC * BR * 2;     // P^T or dS^T tile
-  constexpr int NCH = D / 8;
   constexpr int NKK = D / 16;          // k-steps over d
   constexpr int NDB = D / 32;          // 32-wide column blocks over d
   constexpr int QLPW = 2 * QTILEB / 1024 / 4;  // copies per consumer wave per step (Q and dO)
@@ -518,7 +517,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
-  constexpr int NCH = D / 8;
   constexpr int LOADS = TILEB / 1024;
   constexpr int LPW = LOADS / NW;
   constexpr int NSB = BC / 32;           // 32-key sub-blocks of a tile

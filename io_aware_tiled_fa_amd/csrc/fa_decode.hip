@@ -16,7 +16,7 @@
 //    r = i (H / H_kv) + g), so each key and value is read from HBM once per
 //    group instead of once per query head;
 //  * the split's keys stream through LDS in stages of 128 (double buffered,
-//    direct global -> LDS copies, the forward kernel's swizzle); each of the
+//    direct global -> LDS copies, the forward kernel's layout); each of the
 //    4 waves takes 32 keys of a stage and keeps its own online softmax;
 //  * at the end the waves merge through LDS, and the workgroup writes either
 //    the final row (one split) or the split's normalised partial output and
@@ -85,36 +85,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
     for (int kk = 0; kk < NKK; ++kk) qop[kk] = bf16x8{};
   }
 
-  // ---- LDS read offsets within a wave's 32 keys (the forward kernel's
-  // geometry; the swizzle repeats every 16 rows)
-  int koff[NKK];
-  {
-    const int sw = chunk_swizzle<D>(l32);
+  // ---- LDS read offsets within a wave's 32 keys (stages in the row-group
+  // layout of fa_device.h, as in the forward kernel)
+  int krb[2];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * ROWB + (((2 * kk + h2) ^ sw) << 4);
-  }
-  int voff[2][NDB];
+  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  auto koff = [&](int kk) __attribute__((always_inline)) { return krb[kk & 1] + 256 * (kk >> 1); };
+  int vrb[2];
   {
     const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 4 * h2 + (j >> 2) + 8 * r;
-      const int sw = chunk_swizzle<D>(row);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int ch = 4 * db + 2 * (g & 1) + ((j & 3) >> 1);
-        voff[r][db] = row * ROWB + ((ch ^ sw) << 4) + 8 * (j & 1);
-      }
-    }
+    for (int r = 0; r < 2; ++r)
+      vrb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
   }
   // direct copies: wave copy c = w + NW i fills bytes [1024 c, 1024 c + 1024)
-  // of a stage, lane l the 16-byte slot 64 c + l = row p / NCH, chunk p % NCH
-  uint32_t goff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int p = 64 * (w + NW * i) + l;
-    const int row = p / NCH, ch = p % NCH;
-    goff[i] = (uint32_t)(row * (int)rk + ((ch ^ chunk_swizzle<D>(row)) << 3)) * 2u;
+  // of a stage, lane l the 16-byte slot 64 c + l; copy i reads RSTEP i rows
+  // below copy 0, a multiple of 16 (where the layout repeats), so one
+  // per-lane offset serves all copies
+  constexpr int RSTEP = 64 * NW / NCH;
+  static_assert(RSTEP % 16 == 0, "copies of a wave must keep the row-group layout");
+  uint32_t goff;
+  {
+    int row, piece;
+    rg_slot<D>(64 * w + l, row, piece);
+    goff = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
   // K and V of this (batch, key head): rows 0 .. N_k - 1 at a stride of
   // H_kv d, under 2^32 bytes since B N_k H_kv d < 2^31 (rows past N_k read zero)
@@ -127,8 +121,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds_buf(krs, goff[i], soff, (lds_void*)(kdst + c * 1024));
-      copy16_to_lds_buf(vrs, goff[i], soff, (lds_void*)(vdst + c * 1024));
+      const uint32_t so = soff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
+      copy16_to_lds_buf(krs, goff, so, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(vrs, goff, so, (lds_void*)(vdst + c * 1024));
     }
   };
 
@@ -155,7 +150,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
     constexpr bool MASKED = decltype(MASK)::value;
     bf16x8 kop[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kop[kk] = lds_read16(kt + koff[kk]);
+    for (int kk = 0; kk < NKK; ++kk) kop[kk] = lds_read16(kt + koff(kk));
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) sacc = mfma32(kop[kk], qop[kk], sacc);
@@ -203,8 +198,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
       bf16x8 vop[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x4 v0 = lds_read_tr16(vt + 16 * t * ROWB + voff[0][db]);
-        const bf16x4 v1 = lds_read_tr16(vt + 16 * t * ROWB + voff[1][db]);
+        const bf16x4 v0 = lds_read_tr16(vt + 16 * t * ROWB + 256 * db + vrb[0]);
+        const bf16x4 v1 = lds_read_tr16(vt + 16 * t * ROWB + 256 * db + vrb[1]);
         vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll

@@ -129,18 +129,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
 
 __device__ __forceinline__ bf16x8 lds_read16(const lds_char* p) { return *(const lds_bf16x8*)p; }
 
-// XOR swizzle of the 16-byte chunk index of an LDS tile row.  For 128-wide
-// rows it makes both the 32-row b128 reads of a K tile and the 4-row
-// transpose reads of a V tile hit distinct banks; likewise for 64-wide rows.
-template <int D>
-__device__ __forceinline__ int chunk_swizzle(int row) {
-  if constexpr (D == 128) {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  } else {
-    return ((row >> 2) & 1) | (((row >> 3) & 1) << 1) | (((row >> 1) & 1) << 2);
-  }
-}
-
 // Row-group layout of a [rows][D] bf16 tile in LDS.  The tile is cut into
 // 128-byte blocks of 4 consecutive rows by 2 consecutive 16-byte pieces (16
 // columns): block (rg, pp) of row group rg = row / 4 and piece pair pp sits
