@@ -32,15 +32,6 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
-#ifndef PROD_AHEAD
-#define PROD_AHEAD 3
-#endif
-#ifndef DQ_PIPE
-#define DQ_PIPE 1  // dQ kernel: sub-blocks software-pipelined (dS beside products)
-#endif
-#ifndef CONS_AHEAD
-#define CONS_AHEAD 2
-#endif
 
 namespace fa {
 
@@ -347,7 +338,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pn[4 * g4 + i] = nd[i];
       }
-      constexpr int PD = PROD_AHEAD;  // k-steps the operand reads run ahead
+      constexpr int PD = 3;  // k-steps the operand reads run ahead
       bf16x8 ring[PD + 1][2];
       auto read_rows = [&](int kk, bf16x8 (&dst2)[2]) __attribute__((always_inline)) {
         const int off = krb[kk & 1] + 256 * (kk >> 1);
@@ -444,7 +435,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     // tq (queries 16 tq + 4 h2 + 0..3 and + 8), B = dO / Q columns by
     // transpose reads; operands one product ahead
     constexpr int NP = 2 * NDB;
-    constexpr int CD = CONS_AHEAD;  // products the operand reads run ahead
+    constexpr int CD = 2;  // products the operand reads run ahead
     bf16x8 pa[2], sa[2], go[CD + 1], qo[CD + 1];
     auto read_op = [&](int i) __attribute__((always_inline)) {
       const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
@@ -528,7 +519,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
-  // ---- workgroup -> (batch, head, query tile), as in the forward kernel
+  // ---- workgroup -> (batch, head, query tile): each XCD a contiguous range
+  // of heads (as the dK/dV kernel), the heaviest causal tiles first
   const int nqb = (a.Nq + BR - 1) / BR;
   const int nbh = a.B * a.H;
   const int wg = blockIdx.x;
@@ -632,7 +624,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
 
-#if DQ_PIPE
   // One key tile as two 32-key sub-blocks, software-pipelined so the dS
   // work (VALU) of one sub-block runs beside independent matrix-core
   // products of the same wave:
@@ -725,67 +716,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     dqmm(0, d0, std::true_type{}, s1, p1, d1);
     dqmm(1, d1, std::false_type{}, s1, p1, d1);
   };
-#else
-  auto compute_tile = [&](auto MASK, int kb, const lds_char* __restrict__ kt_lds,
-                          const lds_char* __restrict__ vt_lds) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(MASK)::value;
-    const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;  // last visible key
-    const int lo = qrow + lo_off;                                     // first (banded)
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      // S^T and dP^T of the 32-key sub-block: lane holds [key 8(e/4)+4h2+e%4][query l32];
-      // the K / V operands of k-step kk + 2 are requested before the products of kk
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      bf16x8 ring[3][2];
-      auto read_kv = [&](int kk, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-        const int off = sb * 32 * ROWB + krb[kk & 1] + 256 * (kk >> 1);
-        dst[0] = lds_read16(kt_lds + off);
-        dst[1] = lds_read16(vt_lds + off);
-      };
-      read_kv(0, ring[0]);
-      read_kv(1, ring[1]);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 2 < NKK) read_kv(kk + 2, ring[(kk + 2) % 3]);
-        __builtin_amdgcn_sched_barrier(0);
-        sacc = mfma32(ring[kk % 3][0], qop[kk], sacc);
-        pacc = mfma32(ring[kk % 3][1], gop[kk], pacc);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e), masked above the diagonal
-      uint32_t dspk[8];
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        float p0 = fast_exp2(fmaf(sacc[e], c, nl));
-        float p1 = fast_exp2(fmaf(sacc[e + 1], c, nl));
-        if constexpr (MASKED) {  // key outside the row's band, or key >= N_k
-          const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          p0 = (key > hi || (WIN && key < lo)) ? 0.f : p0;
-          p1 = (key + 1 > hi || (WIN && key + 1 < lo)) ? 0.f : p1;
-        }
-        dspk[e >> 1] = pack_bf16x2(p0 * (pacc[e] + ndr), p1 * (pacc[e + 1] + ndr));
-      }
-      // dQ^T += K^T dS^T over the sub-block's 32 keys, two steps of 16
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const bf16x8 sop = __builtin_bit_cast(bf16x8, u32x4{dspk[4 * tq], dspk[4 * tq + 1], dspk[4 * tq + 2], dspk[4 * tq + 3]});
-        const int t = 2 * sb + tq;
-        bf16x8 kop[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x4 k0 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[0]);
-          const bf16x4 k1 = lds_read_tr16(kt_lds + 16 * t * ROWB + 256 * db + trb[1]);
-          kop[db] = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) dqacc[db] = mfma32(kop[db], sop, dqacc[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-#endif
 
   // MAYMASK: whether the tile can need masking (tiles crossing a band edge,
   // or the ragged last tile); unbanded loops never instantiate the masked
