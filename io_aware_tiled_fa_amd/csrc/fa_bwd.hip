@@ -649,7 +649,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
         p0 = (key > hi || (WIN && key < lo)) ? 0.f : p0;
         p1 = (key + 1 > hi || (WIN && key + 1 < lo)) ? 0.f : p1;
       }
-      dspk[u] = pack_bf16x2(p0 * (pv[e] + ndr), p1 * (pv[e + 1] + ndr));
+      dspk[u] = pack_bf16x2(p0 * pv[e], p1 * pv[e + 1]);
       asm volatile("" : "+v"(dspk[u]));
     };
     // S^T and dP^T of sub-block sb (lane: [key 8(e/4)+4h2+e%4][query l32]);
@@ -658,7 +658,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     auto sdp = [&](int sb, f32x16& sacc, f32x16& pacc, auto PREV, const f32x16& sp, const f32x16& pp,
                    uint32_t (&dsp)[8]) __attribute__((always_inline)) {
       sacc = f32x16{};
-      pacc = f32x16{};
+      // dP^T accumulates onto -D of the lane's row (every element of a lane
+      // is in that row), so dS = P (dP - D) takes one multiply
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pacc[e] = ndr;
       bf16x8 ring[3][2];
       auto read_kv = [&](int kk, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
         const int off = sb * 32 * ROWB + krb[kk & 1] + 256 * (kk >> 1);
