@@ -154,23 +154,27 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     }
 
 
-# Pipe-utilisation counters of the kernels of one step: two rocprofv3 passes
-# (a pass holds at most 8 SQ counters), then a summary into PIPE_FILE.
+# Pipe-utilisation counters of the kernels of one step: three rocprofv3
+# passes (a pass holds at most 8 SQ and 4 TCC counters), then a summary into
+# PIPE_FILE.
 PIPE_PASSES = [
     "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
     "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
     "GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_BF16 TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
 ]
 PIPE_COMMANDS = [
     f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pipe{i} -o p -- "
     "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next" for i, c in enumerate(PIPE_PASSES)
-] + ["python3 bench.py --pipe-summary gpurun_out/pipe0 gpurun_out/pipe1"]
+] + ["python3 bench.py --pipe-summary " + " ".join(f"gpurun_out/pipe{i}" for i in range(len(PIPE_PASSES)))]
 
 
 def pipe_summary(dirs) -> str:
     """Per kernel of the step (last dispatch of each): matrix-core busy and
     co-execution as a share of the cycles of all SIMDs, VALU and LDS issue
-    as a share of wave cycles, LDS busy and bank-conflict cycles per CU."""
+    as a share of wave cycles, LDS busy and bank-conflict cycles per CU; then
+    the bf16 matrix flops the counters saw (512 per MOPS unit) beside the
+    useful flops of the call, and the L2 hit rate."""
     import collections
     import csv
     import glob
@@ -207,6 +211,19 @@ def pipe_summary(dirs) -> str:
             f"{c['SQ_ACTIVE_INST_LDS'] / wc:.1%} | {c['SQ_WAIT_INST_ANY'] / wc:.1%} | "
             f"{c['SQ_LDS_IDX_ACTIVE'] / (g * 256):.1%} | "
             f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%} |")
+    lines += ["", "| kernel | grid threads | MFMA instructions | bf16 matrix TFLOP executed | L2 hit rate |",
+              "|---|---|---|---|---|"]
+    for (k, grid), v in sorted(per.items()):
+        c = {kk.split(":", 1)[1]: x for kk, x in v.items()}
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c:
+            continue
+        hits, miss = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        lines.append(f"| `{k}` | {grid} | {c['SQ_INSTS_VALU_MFMA_BF16']:.4g} | "
+                     f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e12:.4f} | {hits / max(hits + miss, 1):.1%} |")
+    lines += ["", f"Useful flops per call: forward {fwd_flops(FWD) / 1e12:.4f} TFLOP (4 B H N^2 d, halved for "
+              f"causal); backward {bwd_flops(BWD) / 1e12:.4f} TFLOP (2.5 x its forward). The backward kernels "
+              "execute seven products per tile pair against the five of the useful count (S and dP are "
+              "computed once for dK / dV and again for dQ), and whole tiles on the diagonal."]
     return "\n".join(lines)
 
 
@@ -314,7 +331,7 @@ def main(argv=None):
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--stats-summary", metavar="DIR",
                     help="summarise the STATS_COMMANDS kernel trace into " + os.path.relpath(STATS_FILE, ROOT))
-    ap.add_argument("--pipe-summary", nargs=2, metavar=("PASS0_DIR", "PASS1_DIR"),
+    ap.add_argument("--pipe-summary", nargs="+", metavar="PASS_DIR",
                     help="summarise the PIPE_COMMANDS counter passes into " + os.path.relpath(PIPE_FILE, ROOT))
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the forward kernel's HBM counter summary from two rocprofv3 runs")
@@ -326,8 +343,8 @@ def main(argv=None):
             f.write("# rocprofv3 kernel summary\n\n"
                     "Workloads: fa_fwd on B=1 H=32 N=32768 d=128 causal (the fwd_kernel launch of 2752 "
                     "workgroups of 768 threads; the smaller fwd_kernel launch is the setup forward of the "
-                    "backward batch) and fa_bwd on B=4 H=16 N=4096 d=128 causal (bwd_pre_kernel, "
-                    "bwd_main_kernel = dK/dV, bwd_dq_kernel = dQ).\n\n"
+                    "backward batch) and fa_bwd on B=4 H=16 N=4096 d=128 causal (bwd_dq_kernel = dQ "
+                    "and the row terms, then bwd_main_kernel = dK/dV).\n\n"
                     f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root, MI355X, ROCm 7.2):"
                     "\n\n```\n" + "\n".join(STATS_COMMANDS) + "\n```\n\n" + table + "\n")
         print(table)
@@ -338,7 +355,7 @@ def main(argv=None):
         with open(PIPE_FILE, "w") as f:
             f.write("# Pipe utilisation of the step's kernels (rocprofv3 counters)\n\n"
                     "One step of bench.py (long-context causal forward, then the backward batch), "
-                    "two counter passes, last dispatch of each kernel. Shares of SIMD cycles assume "
+                    "three counter passes, last dispatch of each kernel. Shares of SIMD cycles assume "
                     "256 CUs x 4 SIMDs in 8 XCDs; the shader clock under load is about 1.75-1.9 GHz, "
                     "against the 2.4 GHz of the quoted peak.\n\n"
                     f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root):\n\n```\n"

@@ -11,19 +11,20 @@
 // P_ij = exp(s_ij - L_i), and the softmax Jacobian term sum_j P_ij dP_ij
 // equals D_i = sum_c dO_ic O_ic, so no row of P is ever needed whole.
 //
-// Three kernels on one stream, none of them atomic, so the gradients are
-// the same bit for bit on every run:
-//  1. bwd_pre: -D_i = -dO_i . O_i and -L_i log2(e) per row (float32);
+// Two kernels on one stream, none of them atomic, so the gradients are the
+// same bit for bit on every run:
+//  1. bwd_dq (dQ): one workgroup per query tile, walking the key tiles like
+//     the forward kernel and recomputing S and dP; dQ is summed in
+//     registers and written once.  Each wave also forms the row terms of
+//     its rows, -D_i = -dO_i . O_i and -L_i log2(e) (float32), and writes
+//     them to the workspace for the second kernel;
 //  2. bwd_main (dK, dV): one workgroup of 8 waves per 128-key block of one
 //     (batch, key head).  Four producer waves recompute S = Q K^T, P and
 //     dS = P (dP - D) for 32 keys each against 32-query blocks staged in
 //     LDS; the consumer wave on the same SIMD adds P^T dO and dS^T Q into
 //     dV and dK, one block behind.  The walk covers every query block of
 //     every query head that reads this key head (grouped-query attention)
-//     whose rows see a key of the block;
-//  3. bwd_dq (dQ): one workgroup per query tile, walking the key tiles like
-//     the forward kernel and recomputing S and dP; dQ is summed in
-//     registers and written once.
+//     whose rows see a key of the block.
 // Masks: key j is visible to query i iff i + off - wl <= j <= i + off + wr
 // (off = N_k - N_q), the forward kernel's band.
 // All products run on v_mfma_f32_32x32x16_bf16.
@@ -36,45 +37,7 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. row terms: -D_i = -sum_c dO_ic O_ic and -L_i log2(e), float32.  One
-//    16-lane group per (b, n, h) row for d = 128 (8-lane for d = 64); 256
-//    threads per block.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;            // lanes per row, 8 bf16 each
-  constexpr int RPB = 256 / LPR;        // rows per block
-  const int t = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + t / LPR;  // index over (b, n, h)
-  const int sub = t % LPR;
-  const long nrows = (long)a.B * a.Nq * a.H;
-  float acc = 0.f;
-  if (row < nrows) {
-    const size_t off = (size_t)row * D + 8 * sub;
-    const u32x4 ov = *(const u32x4*)(a.o + off);
-    const u32x4 gv = *(const u32x4*)(a.dO + off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float o0 = __builtin_bit_cast(float, ov[i] << 16), o1 = __builtin_bit_cast(float, ov[i] & 0xFFFF0000u);
-      const float g0 = __builtin_bit_cast(float, gv[i] << 16), g1 = __builtin_bit_cast(float, gv[i] & 0xFFFF0000u);
-      acc = fmaf(o0, g0, acc);
-      acc = fmaf(o1, g1, acc);
-    }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (row < nrows && sub == 0) {
-    const int h = (int)(row % a.H);
-    const long bn = row / a.H;
-    const int n = (int)(bn % a.Nq);
-    const int b = (int)(bn / a.Nq);
-    const size_t r = ((size_t)b * a.H + h) * a.Nq + n;
-    a.drow[r] = -acc;
-    a.drow[(size_t)a.B * a.H * a.Nq + r] = -a.lse[r] * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dK / dV kernel: one workgroup of 8 waves per 128-key block, walking the
+// dK / dV kernel: one workgroup of 8 waves per 128-key block, walking the
 //    query blocks of 32 rows.  The waves specialise: wave w < 4 produces and
 //    wave w + 4 (on the same SIMD) consumes for key group kg = w, keys
 //    32 kg .. 32 kg + 31 of the block.  In step t:
@@ -493,7 +456,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ kernel: one workgroup of NW waves per (batch, head, query tile of
+// dQ kernel: one workgroup of NW waves per (batch, head, query tile of
 //    32 NW rows), walking the key tiles like the forward kernel (K and V
 //    tiles double-buffered in LDS by direct copies).  Everything is computed
 //    transposed so lane l32 of a wave owns one query row:
@@ -555,23 +518,42 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbase = a.k + kv_off;
   const __bf16* vbase = a.v + kv_off;
 
-  // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..), row terms
+  // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..),
+  // and the row terms: D = dO . O over the lane's half of the row, then
+  // both halves; -D and -L log2(e) also go to the workspace for the dK / dV
+  // kernel, which runs after this one
   bf16x8 qop[NKK], gop[NKK];
   float nl = 0.f, ndr = 0.f;  // -L log2(e) and -D of this lane's row
+  float dpart = 0.f;
   if (row_valid) {
     const __bf16* qr = a.q + q_off + (size_t)qrow * rs + 8 * h2;
     const __bf16* gr = a.dO + q_off + (size_t)qrow * rs + 8 * h2;
+    const __bf16* orow = a.o + q_off + (size_t)qrow * rs + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       qop[kk] = *(const bf16x8*)(qr + 16 * kk);
       gop[kk] = *(const bf16x8*)(gr + 16 * kk);
+      const u32x4 ov = *(const u32x4*)(orow + 16 * kk);
+      const u32x4 gv = __builtin_bit_cast(u32x4, gop[kk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dpart = fmaf(__builtin_bit_cast(float, ov[i] << 16), __builtin_bit_cast(float, gv[i] << 16), dpart);
+        dpart = fmaf(__builtin_bit_cast(float, ov[i] & 0xFFFF0000u), __builtin_bit_cast(float, gv[i] & 0xFFFF0000u), dpart);
+      }
     }
-    const size_t r = ((size_t)b * a.H + h) * a.Nq + qrow;
-    ndr = a.drow[r];
-    nl = a.drow[(size_t)a.B * a.H * a.Nq + r];
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qop[kk] = gop[kk] = bf16x8{};
+  }
+  const float dsum = sum_cross_half(dpart);
+  if (row_valid) {
+    const size_t r = ((size_t)b * a.H + h) * a.Nq + qrow;
+    ndr = -dsum;
+    nl = -a.lse[r] * kLog2e;
+    if (h2 == 0) {
+      a.drow[r] = ndr;
+      a.drow[(size_t)a.B * a.H * a.Nq + r] = nl;
+    }
   }
 
   // ---- per-lane LDS offsets (K and V tiles in the row-group layout)
@@ -781,23 +763,15 @@ template <int D, bool BAND, bool WIN>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   void* args[] = {(void*)&a};
   {
-    const long rows = (long)a.B * a.Nq * a.H;
-    const int rpb = 256 / (D / 8);
-    dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-    hipError_t e = hipLaunchKernel((const void*)bwd_pre_kernel<D>, grid, dim3(256), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  {
-    dim3 grid((unsigned)(a.B * a.Hkv * ((a.Nk + 127) / 128)));
-    hipError_t e = hipLaunchKernel((const void*)bwd_main_kernel<D, BAND, WIN>, grid, dim3(512), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  {
+    // dQ, and the row terms of every query row into the workspace
     constexpr int NW = D == 128 ? 8 : 4;
     constexpr int BR = NW * 32;
     dim3 grid((unsigned)(a.B * a.H * ((a.Nq + BR - 1) / BR)));
-    return hipLaunchKernel((const void*)bwd_dq_kernel<D, NW, 64, BAND, WIN>, grid, dim3(NW * 64), args, 0, stream);
+    hipError_t e = hipLaunchKernel((const void*)bwd_dq_kernel<D, NW, 64, BAND, WIN>, grid, dim3(NW * 64), args, 0, stream);
+    if (e != hipSuccess) return e;
   }
+  dim3 grid((unsigned)(a.B * a.Hkv * ((a.Nk + 127) / 128)));
+  return hipLaunchKernel((const void*)bwd_main_kernel<D, BAND, WIN>, grid, dim3(512), args, 0, stream);
 }
 
 template <int D>
