@@ -38,17 +38,19 @@ namespace fa {
 
 // ---------------------------------------------------------------------------
 // dK / dV kernel: one workgroup of 8 waves per 128-key block, walking the
-//    query blocks of 32 rows.  The waves specialise: wave w < 4 produces and
-//    wave w + 4 (on the same SIMD) consumes for key group kg = w, keys
-//    32 kg .. 32 kg + 31 of the block.  In step t:
+//    query blocks of 32 rows.  The waves specialise: wave w < 4 produces for
+//    key group w (keys 32 w .. 32 w + 31 of the block); waves 4 and 5 add dV
+//    for keys 0-63 and 64-127, waves 6 and 7 dK for the same halves (each
+//    transpose read of dO or Q feeds two products).  In step t:
 //      producer (block t):     S = Q K^T and dP - D = dO V^T - D      16 products
 //                              P = exp2(S c - L log2 e) (masked), dS = P (dP - D)
 //                              P^T, dS^T -> LDS (bf16)
-//      consumer (block t - 1): dV += P^T dO, dK += dS^T Q over its 32 rows     16 products
-//    so the producer's softmax runs beside the consumer's matrix products.
-//    One barrier per step; Q / dO tiles are triple-buffered (the producer
-//    reads block t, the consumer block t - 1, the copies fill block t + 1)
-//    and the P^T / dS^T tiles double-buffered.
+//      consumer (block t - 1): dV += P^T dO or dK += dS^T Q over its 32 rows   16 products
+//    so the producers' softmax runs beside the consumers' matrix products;
+//    every SIMD holds one producer and one consumer.  One barrier per step;
+//    Q / dO tiles and row terms are in four buffers (the producer's products
+//    read block t + 1, the consumers block t - 1, the copies fill block
+//    t + 2) and the P^T / dS^T tiles double-buffered.
 //
 // P^T / dS^T tiles: 128 key rows of 32 queries (64 B), in 8-byte chunks of 4
 // queries, chunk c of row r at c ^ ((r >> 2) & 7): conflict-free for the
@@ -383,36 +385,49 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     return;
   }
 
-  // ---- consumer: dV^T += dO^T P and dK^T += Q^T dS over the block's rows,
-  // two steps of 16 queries; lane holds [key 8(e/4)+4h2+e%4][d = 32 db + l32]
-  f32x16 dvacc[NDB], dkacc[NDB];
+  // ---- consumers: waves 4 and 5 add dV^T += dO^T P for keys 0-63 and
+  // 64-127 of the block, waves 6 and 7 dK^T += Q^T dS for the same halves.
+  // Each transpose read of dO or Q then feeds two products (one per 32-key
+  // group of the half).  Accumulators: [group of the half][db], lane holds
+  // [key 8(e/4)+4h2+e%4][d = 32 db + l32].
+  const int kh = w & 1;             // key half of this consumer
+  const int kw2 = kb + 64 * kh;     // its first key
+  f32x16 acc[2][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dvacc[db] = dkacc[db] = f32x16{};
-  auto consume = [&](int qi, const lds_char* __restrict__ qt, const lds_char* __restrict__ gt,
-                     const lds_char* __restrict__ pt, const lds_char* __restrict__ dst)
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[g][db] = f32x16{};
+  // P^T / dS^T chunks of the two groups: key rows 32 (2 kh + g) + l32,
+  // queries 8 g4 + 4 h2 at pb[g] ^ (16 g4)
+  int pb[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) pb[g] = pt_off(32 * (2 * kh + g) + l32, 4 * h2);
+  // DV: dO and P^T (dV), else Q and dS^T (dK); a compile-time choice, so
+  // every read names its LDS buffer
+  auto consume = [&](auto DV, int qi, const lds_char* __restrict__ xt, const lds_char* __restrict__ pt)
       __attribute__((always_inline)) {
-    // P = dS = 0 for this block: every row's band misses the group's keys
-    if ((BAND && qi * BR + BR - 1 + hi_off < kw) || (WIN && qi * BR + lo_off > kw + 31)) return;
+    // P = dS = 0 for this block: every row's band misses the half's keys
+    if ((BAND && qi * BR + BR - 1 + hi_off < kw2) || (WIN && qi * BR + lo_off > kw2 + 63)) return;
     typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-    // product i = (tq, db): A = P^T / dS^T chunks of the 16 queries of step
-    // tq (queries 16 tq + 4 h2 + 0..3 and + 8), B = dO / Q columns by
-    // transpose reads; operands one product ahead
+    // product pair i = (tq, db): B = dO / Q columns (transpose reads, CD
+    // pairs ahead), A = the P^T / dS^T chunks of the 16 queries of step tq
+    // for each group
     constexpr int NP = 2 * NDB;
-    constexpr int CD = 2;  // products the operand reads run ahead
-    bf16x8 pa[2], sa[2], go[CD + 1], qo[CD + 1];
+    constexpr int CD = 2;
+    bf16x8 pa[2][2], xo[CD + 1];
     auto read_op = [&](int i) __attribute__((always_inline)) {
       const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
       if (db == 0) {
-        const int o0 = pbase ^ (32 * tq), o1 = pbase ^ (32 * tq + 16);
-        const u32x2 p0 = *(const lds_u32x2*)(pt + o0), p1 = *(const lds_u32x2*)(pt + o1);
-        const u32x2 s0 = *(const lds_u32x2*)(dst + o0), s1 = *(const lds_u32x2*)(dst + o1);
-        pa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
-        sa[tq & 1] = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const u32x2 p0 = *(const lds_u32x2*)(pt + (pb[g] ^ (32 * tq)));
+          const u32x2 p1 = *(const lds_u32x2*)(pt + (pb[g] ^ (32 * tq + 16)));
+          pa[g][tq & 1] = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
+        }
       }
       const int o0 = 16 * tq * ROWB + 256 * db + trb[0];
       const int o1 = 16 * tq * ROWB + 256 * db + trb[1];
-      go[s] = __builtin_shufflevector(lds_read_tr16(gt + o0), lds_read_tr16(gt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
-      qo[s] = __builtin_shufflevector(lds_read_tr16(qt + o0), lds_read_tr16(qt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+      xo[s] = __builtin_shufflevector(lds_read_tr16(xt + o0), lds_read_tr16(xt + o1), 0, 1, 2, 3, 4, 5, 6, 7);
     };
 #pragma unroll
     for (int i = 0; i < CD && i < NP; ++i) read_op(i);
@@ -422,37 +437,50 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
       if (i + CD < NP) read_op(i + CD);
       __builtin_amdgcn_sched_barrier(0);
       const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
-      dvacc[db] = mfma32(pa[tq & 1], go[s], dvacc[db]);
-      dkacc[db] = mfma32(sa[tq & 1], qo[s], dkacc[db]);
+      acc[0][db] = mfma32(pa[0][tq & 1], xo[s], acc[0][db]);
+      acc[1][db] = mfma32(pa[1][tq & 1], xo[s], acc[1][db]);
     }
   };
-  auto cstep = [&](auto T, int t) __attribute__((always_inline)) {
+  const bool half_active = kw2 < a.Nk;
+  auto cstep = [&](auto DV, auto T, int t) __attribute__((always_inline)) {
     constexpr int T4 = decltype(T)::value;
     step_barrier();
     if (t + 2 < nv) issue_next(IC<T4 + 2>{});
-    if (group_active && t > 0)
-      consume(qbuf[(T4 + 3) & 3], QT(IC<T4 + 3>{}), GT(IC<T4 + 3>{}), PT(IC<T4 + 1>{}), DT(IC<T4 + 1>{}));
-  };
-  for (int t = 0; t < nsteps; t += 4) {
-    cstep(IC<0>{}, t);
-    if (t + 1 < nsteps) cstep(IC<1>{}, t + 1);
-    if (t + 2 < nsteps) cstep(IC<2>{}, t + 2);
-    if (t + 3 < nsteps) cstep(IC<3>{}, t + 3);
-  }
-
-  // ---- consumer epilogue: dK = scale dK_acc, dV = dV_acc
-  if (!group_active) return;
-  const float scale = a.scale;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kr = kw + 8 * (e >> 2) + 4 * h2 + (e & 3);
-      if (kr >= a.Nk) continue;
-      const size_t o = kv_off + (size_t)kr * rk + 32 * db + l32;
-      a.dk[o] = (__bf16)(dkacc[db][e] * scale);
-      a.dv[o] = (__bf16)(dvacc[db][e]);
+    if (half_active && t > 0) {
+      if constexpr (decltype(DV)::value)
+        consume(DV, qbuf[(T4 + 3) & 3], GT(IC<T4 + 3>{}), PT(IC<T4 + 1>{}));
+      else
+        consume(DV, qbuf[(T4 + 3) & 3], QT(IC<T4 + 3>{}), DT(IC<T4 + 1>{}));
     }
+  };
+  auto walk = [&](auto DV) __attribute__((always_inline)) {
+    for (int t = 0; t < nsteps; t += 4) {
+      cstep(DV, IC<0>{}, t);
+      if (t + 1 < nsteps) cstep(DV, IC<1>{}, t + 1);
+      if (t + 2 < nsteps) cstep(DV, IC<2>{}, t + 2);
+      if (t + 3 < nsteps) cstep(DV, IC<3>{}, t + 3);
+    }
+  };
+  const bool dv_role = w < 6;
+  if (dv_role)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+
+  // ---- consumer epilogue: dV = dV_acc, or dK = scale dK_acc
+  if (!half_active) return;
+  const float f = dv_role ? 1.0f : a.scale;
+  __bf16* out = dv_role ? a.dv : a.dk;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kr = kw2 + 32 * g + 8 * (e >> 2) + 4 * h2 + (e & 3);
+        if (kr >= a.Nk) continue;
+        out[kv_off + (size_t)kr * rk + 32 * db + l32] = (__bf16)(acc[g][db][e] * f);
+      }
 }
 
 // ---------------------------------------------------------------------------
