@@ -42,15 +42,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// The same product with the accumulator pinned to AGPRs.  For accumulators
-// only the matrix cores touch until an epilogue, this keeps them out of the
-// VGPRs the rest of the kernel needs.  (Arithmetic only: no memory operand.)
-__device__ __forceinline__ void mfma32_agpr(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
-__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
-
 // max(x[l], x[l ^ 32]) in every lane
 __device__ __forceinline__ float max_cross_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -75,12 +66,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// 16-byte asynchronous copy global -> LDS.  Lane l writes bytes
-// [lds + 16 l, lds + 16 l + 16); lds must be the same in every lane.
-__device__ __forceinline__ void copy16_to_lds(const void* g, lds_void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
 // Buffer resource over `bytes` bytes from `base` (raw, untyped: the fourth
 // descriptor word of the gfx9 family).  Accesses past `bytes` read zero.
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
@@ -99,26 +84,14 @@ __device__ __forceinline__ void copy16_to_lds_buf(buf_rsrc r, uint32_t voff, uin
 // wait until every outstanding vector-memory load of this wave has landed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Workgroup barrier without the memory fence of __syncthreads().  The fence
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
 // makes the compiler wait for every outstanding vector-memory operation
-// (prefetch copies, atomics) before the barrier; these barriers instead wait
-// only for what they publish.  The empty asm statements keep the compiler
-// from moving memory accesses across the barrier.
-//  * barrier_lds: this wave's LDS writes (ds_write) are complete;
-//  * barrier_vmem<N>: all but the N most recent vector-memory operations of
-//    this wave (which retire in issue order) are complete, e.g. its LDS
-//    copies of a tile while its later atomics may still be in flight.
+// (prefetch copies) before the barrier; this one waits only for this wave's
+// LDS writes (ds_write), which is what it publishes.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt / expcnt wait
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void barrier_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
