@@ -21,8 +21,9 @@
 //  2. bwd_main (dK, dV): one workgroup of 8 waves per 128-key block of one
 //     (batch, key head).  Four producer waves recompute S = Q K^T, P and
 //     dS = P (dP - D) for 32 keys each against 32-query blocks staged in
-//     LDS; the consumer wave on the same SIMD adds P^T dO and dS^T Q into
-//     dV and dK, one block behind.  The walk covers every query block of
+//     LDS; four consumer waves, one beside each producer on its SIMD, add
+//     P^T dO into dV (two of them, 64 keys each) or dS^T Q into dK (the
+//     other two), one block behind.  The walk covers every query block of
 //     every query head that reads this key head (grouped-query attention)
 //     whose rows see a key of the block.
 // Masks: key j is visible to query i iff i + off - wl <= j <= i + off + wr
