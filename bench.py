@@ -255,11 +255,15 @@ def stats_summary(d: str) -> str:
         out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                    f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
     out += ["", "## per launch shape (from the kernel trace)", "",
-            "| kernel | workgroups | threads / WG | VGPRs | LDS bytes | dispatches | avg ms | min ms | max ms |",
-            "|---|---|---|---|---|---|---|---|---|"]
+            "| kernel | workgroups | threads / WG | VGPRs | LDS bytes | dispatches | avg ms | avg ms after the first "
+            "| median ms | min ms | max ms |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (k, wgs, wgsz, vg, lds), v in per.items():
+        rest = v[1:] or v
         out.append(f"| `{k}` | {wgs} | {wgsz} | {vg} | {lds} | {len(v)} | {sum(v) / len(v):.4f} | "
-                   f"{min(v):.4f} | {max(v):.4f} |")
+                   f"{sum(rest) / len(rest):.4f} | {sorted(v)[len(v) // 2]:.4f} | {min(v):.4f} | {max(v):.4f} |")
+    out += ["", "The first dispatch of a kernel in the process runs cold (code and caches); bench.py's "
+            "roofline times the launches after its warmup, so it compares with the average after the first."]
     return "\n".join(out)
 
 
