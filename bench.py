@@ -195,9 +195,10 @@ def pipe_summary(dirs) -> str:
                 if did == last[key]:
                     per[key][d + ":" + r["Counter_Name"]] = per[key].get(d + ":" + r["Counter_Name"], 0.0) + \
                         float(r["Counter_Value"])
-    lines = ["| kernel | grid threads | cycles (per XCD) | MFMA busy | MFMA+VALU co-exec | VALU issue / wave | "
+                    per[key][d + ":ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    lines = ["| kernel | grid threads | cycles (per XCD) | clock GHz | MFMA busy | MFMA+VALU co-exec | VALU issue / wave | "
              "LDS issue / wave | wait / wave | LDS busy / CU | LDS bank-conflict cycles / LDS busy |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (k, grid), v in sorted(per.items()):
         c = {kk.split(":", 1)[1]: x for kk, x in v.items()}
         if "SQ_WAVE_CYCLES" not in c or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
@@ -205,8 +206,10 @@ def pipe_summary(dirs) -> str:
         g = c["GRBM_GUI_ACTIVE"] / 8  # per XCD
         simd = g * 1024               # 256 CUs x 4 SIMDs over 8 XCDs
         wc = c["SQ_WAVE_CYCLES"]
+        ns = c.get("ns", 0.0)
+        clk = f"{g / ns:.2f}" if ns > 0 else "-"  # busy cycles of one XCD over the dispatch's duration
         lines.append(
-            f"| `{k}` | {grid} | {g:.3g} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.1%} | "
+            f"| `{k}` | {grid} | {g:.3g} | {clk} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.1%} | "
             f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd:.1%} | {c['SQ_ACTIVE_INST_VALU'] / wc:.1%} | "
             f"{c['SQ_ACTIVE_INST_LDS'] / wc:.1%} | {c['SQ_WAIT_INST_ANY'] / wc:.1%} | "
             f"{c['SQ_LDS_IDX_ACTIVE'] / (g * 256):.1%} | "
