@@ -504,11 +504,37 @@ def main(argv=None):
     if not args.no_next:
         print("# extension configurations", file=sys.stderr, flush=True)
         rec["next"] = measure_next(binding, torch, dev)
+        print("# dense bf16 GEMM of the vendor library on the same GPU (context)", file=sys.stderr, flush=True)
+        rec["context_gemm"] = library_gemm_rate(torch, dev)
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(fin, bin_, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def library_gemm_rate(torch, dev, n: int = 8192, reps: int = 150) -> dict:
+    """torch.matmul of two n x n bf16 matrices (hipBLASLt) on the same GPU:
+    what a plain dense product sustains on this board, whose clock settles
+    where its power limit holds it, timed over ~0.1 s of back-to-back calls
+    like the attention steps.  Context for the percentages above (all
+    against the 2.5 PFLOP/s published peak); no part of the attention path."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(30):  # (the library picks its kernel on the first calls)
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del c
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n} (vendor library)", "ms": round(ms, 4),
+            "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def measure_next(binding, torch, dev, reps: int = 7) -> dict:
