@@ -54,13 +54,17 @@ namespace fa {
 //    t + 2) and the P^T / dS^T tiles double-buffered.
 //
 // P^T / dS^T tiles: 128 key rows of 32 queries (64 B), in 8-byte chunks of 4
-// queries, chunk c of row r at c ^ ((r >> 2) & 7): conflict-free for the
-// 32-row chunk writes and reads of a key group.
+// queries, chunk c of row r at c ^ s(r) with s(r) = 4 r3 + 2 r2 + (r1 ^ r4)
+// (r_i the bits of r).  The 32-row chunk writes and reads of a key group are
+// 8-byte accesses, which the LDS serves 16 lanes at a time over 32 banks:
+// any 16 consecutive rows then hit 16 distinct bank pairs (and any 32 rows
+// 32 pairs of 64 banks).
 template <int I>
 using IC = std::integral_constant<int, I>;
 
 __device__ __forceinline__ int pt_off(int row, int q) {
-  return row * 64 + (((q >> 2) ^ ((row >> 2) & 7)) << 3) + 2 * (q & 3);
+  const int s = ((row >> 1) & 6) | (((row >> 1) ^ (row >> 4)) & 1);
+  return row * 64 + (((q >> 2) ^ s) << 3) + 2 * (q & 3);
 }
 
 template <int D, bool BAND, bool WIN>
