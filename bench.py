@@ -45,8 +45,12 @@ PIPE_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_kernels_mfma_lds_counters.md
 FWD_KERNEL = "fwd_kernel<128, 12, 64, true, false>"
 FWD_KERNEL_DESC = "fwd_kernel<128,12,64,true,false> (12 waves, 384 query rows per workgroup, 64-key tiles)"
 FWD_ROWS_PER_WG, FWD_THREADS_PER_WG = 384, 768
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
+CSRC = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc")
+# the forward kernel's sources (the HBM counter record is tied to these) and
+# every kernel source (the kernel-trace and pipe summaries cover all kernels)
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
+ALL_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                      ("fa_api.hip", "fa_bwd.hip", "fa_decode.hip", "fa_device.h", "fa_fwd.hip", "fa_kernels.h")]
 
 
 def fwd_flops(c) -> float:
@@ -80,9 +84,9 @@ def visible_pairs(Nq: int, Nk: int, causal: bool, window: int = 0) -> int:
     return int(np.maximum(hi - lo + 1, 0).sum())
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(paths=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if paths is None else paths):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -352,7 +356,8 @@ def main(argv=None):
                     "workgroups of 768 threads; the smaller fwd_kernel launch is the setup forward of the "
                     "backward batch) and fa_bwd on B=4 H=16 N=4096 d=128 causal (bwd_dq_kernel = dQ "
                     "and the row terms, then bwd_main_kernel = dK/dV).\n\n"
-                    f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root, MI355X, ROCm 7.2):"
+                    f"Kernel sources hash (every file under csrc/): `{kernel_source_hash(ALL_KERNEL_SOURCES)}`"
+                    "\n\nCommands (repo root, MI355X, ROCm 7.2):"
                     "\n\n```\n" + "\n".join(STATS_COMMANDS) + "\n```\n\n" + table + "\n")
         print(table)
         return 0
@@ -363,9 +368,11 @@ def main(argv=None):
             f.write("# Pipe utilisation of the step's kernels (rocprofv3 counters)\n\n"
                     "One step of bench.py (long-context causal forward, then the backward batch), "
                     "three counter passes, last dispatch of each kernel. Shares of SIMD cycles assume "
-                    "256 CUs x 4 SIMDs in 8 XCDs; the shader clock under load is about 1.75-1.9 GHz, "
-                    "against the 2.4 GHz of the quoted peak.\n\n"
-                    f"Kernel sources hash: `{kernel_source_hash()}`\n\nCommands (repo root):\n\n```\n"
+                    "256 CUs x 4 SIMDs in 8 XCDs; the clock column is the shader clock each dispatch "
+                    "held (busy cycles of an XCD over its duration), against the 2.4 GHz of the "
+                    "quoted peak.\n\n"
+                    f"Kernel sources hash (every file under csrc/): `{kernel_source_hash(ALL_KERNEL_SOURCES)}`"
+                    "\n\nCommands (repo root):\n\n```\n"
                     + "\n".join(PIPE_COMMANDS) + "\n```\n\n" + table + "\n")
         print(table)
         return 0
