@@ -48,9 +48,10 @@ FWD_ROWS_PER_WG, FWD_THREADS_PER_WG = 384, 768
 CSRC = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc")
 # the forward kernel's sources (the HBM counter record is tied to these) and
 # every kernel source (the kernel-trace and pipe summaries cover all kernels)
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_layout.h")]
 ALL_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
-                      ("fa_api.hip", "fa_bwd.hip", "fa_decode.hip", "fa_device.h", "fa_fwd.hip", "fa_kernels.h")]
+                      ("fa_api.hip", "fa_bwd.hip", "fa_decode.hip", "fa_device.h", "fa_fwd.hip", "fa_kernels.h",
+                       "fa_layout.h")]
 
 
 def fwd_flops(c) -> float:

@@ -53,19 +53,10 @@ namespace fa {
 //    read block t + 1, the consumers block t - 1, the copies fill block
 //    t + 2) and the P^T / dS^T tiles double-buffered.
 //
-// P^T / dS^T tiles: 128 key rows of 32 queries (64 B), in 8-byte chunks of 4
-// queries, chunk c of row r at c ^ s(r) with s(r) = 4 r3 + 2 r2 + (r1 ^ r4)
-// (r_i the bits of r).  The 32-row chunk writes and reads of a key group are
-// 8-byte accesses, which the LDS serves 16 lanes at a time over 32 banks:
-// any 16 consecutive rows then hit 16 distinct bank pairs (and any 32 rows
-// 32 pairs of 64 banks).
+// P^T / dS^T tiles: 128 key rows of 32 queries in the layout of pt_off
+// (fa_layout.h).
 template <int I>
 using IC = std::integral_constant<int, I>;
-
-__device__ __forceinline__ int pt_off(int row, int q) {
-  const int s = ((row >> 1) & 6) | (((row >> 1) ^ (row >> 4)) & 1);
-  return row * 64 + (((q >> 2) ^ s) << 3) + 2 * (q & 3);
-}
 
 template <int D, bool BAND, bool WIN>
 __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
@@ -147,16 +138,12 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // krb[kk & 1] + 256 (kk / 2)
   int krb[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  for (int par = 0; par < 2; ++par) krb[par] = rg_row_base<D>(l, par);
   // consumer transpose reads: rows 4 h2 + j/4 (+8 r) of a 16-row step, columns
   // 32 db + 16 (g&1) + 4 (j&3), at trb[r] + 256 db
   int trb[2];
-  {
-    const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      trb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
-  }
+  for (int r = 0; r < 2; ++r) trb[r] = rg_tr_base<D>(l, r);
   // P^T / dS^T chunk of this lane: key row 32 kg + l32, queries 8 g4 + 4 h2 at
   // pbase ^ (16 g4)
   const int pbase = pt_off(32 * kg + l32, 4 * h2);
@@ -594,16 +581,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   // krb[kk & 1] + 256 (kk / 2) + sb 32 ROWB
   int krb[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  for (int par = 0; par < 2; ++par) krb[par] = rg_row_base<D>(l, par);
   // K^T by transpose reads: rows 16 t + 4 h2 + j/4 (+8 r), columns
   // 32 db + 16 (g&1) + 4 (j&3), at trb[r] + 256 db + 16 t ROWB
   int trb[2];
-  {
-    const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      trb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
-  }
+  for (int r = 0; r < 2; ++r) trb[r] = rg_tr_base<D>(l, r);
   // (byte offsets, one unsigned 32-bit value per copy, into buffer resources
   // over this head's K and V rows, sized as in the forward kernel)
   uint32_t goff[LPW];

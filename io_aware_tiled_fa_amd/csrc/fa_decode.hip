@@ -89,15 +89,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
   // layout of fa_device.h, as in the forward kernel)
   int krb[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  for (int par = 0; par < 2; ++par) krb[par] = rg_row_base<D>(l, par);
   auto koff = [&](int kk) __attribute__((always_inline)) { return krb[kk & 1] + 256 * (kk >> 1); };
   int vrb[2];
-  {
-    const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      vrb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
-  }
+  for (int r = 0; r < 2; ++r) vrb[r] = rg_tr_base<D>(l, r);
   // direct copies: wave copy c = w + NW i fills bytes [1024 c, 1024 c + 1024)
   // of a stage, lane l the 16-byte slot 64 c + l; copy i reads RSTEP i rows
   // below copy 0, a multiple of 16 (where the layout repeats), so one

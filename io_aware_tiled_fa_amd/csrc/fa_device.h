@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_layout.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -101,32 +103,5 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const lds_char* p) { return *(const lds_bf16x8*)p; }
-
-// Row-group layout of a [rows][D] bf16 tile in LDS.  The tile is cut into
-// 128-byte blocks of 4 consecutive rows by 2 consecutive 16-byte pieces (16
-// columns): block (rg, pp) of row group rg = row / 4 and piece pair pp sits
-// at (rg D/16 + (pp ^ ((rg >> 1) & 1))) * 128, the rows of a block 32 bytes
-// apart, and the two pieces of a pair swapped when rg is odd.  Then
-//  * the 4 rows x 16 columns that a 16-lane group reads with
-//    ds_read_b64_tr_b16 form one block, 128 contiguous bytes;
-//  * one 16-byte piece of 16 consecutive rows lands in 16 different groups
-//    of 4 banks, so 16-byte reads of a column of pieces are conflict free;
-//  * offsets split into a per-lane base plus compile-time steps: 256 bytes
-//    per 32 columns, 32 ROWB per 32 rows, and for the pieces 2 kk + h2 of
-//    one row a base per parity of kk plus 256 (kk / 2).
-template <int D>
-__device__ __forceinline__ int rg_off(int row, int piece) {
-  const int rg = row >> 2;
-  const int pp = (piece >> 1) ^ ((rg >> 1) & 1);
-  return (rg * (D / 16) + pp) * 128 + (row & 3) * 32 + (((piece & 1) ^ (rg & 1)) << 4);
-}
-// the row and piece stored at 16-byte slot `slot` of the tile (the inverse)
-template <int D>
-__device__ __forceinline__ void rg_slot(int slot, int& row, int& piece) {
-  const int blk = slot >> 3, w = slot & 7;
-  const int rg = blk / (D / 16), pp = (blk % (D / 16)) ^ ((rg >> 1) & 1);
-  row = 4 * rg + (w >> 1);
-  piece = 2 * pp + ((w & 1) ^ (rg & 1));
-}
 
 }  // namespace fa

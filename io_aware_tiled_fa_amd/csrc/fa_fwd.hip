@@ -133,18 +133,14 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
   // krb[kk & 1] + 256 (kk / 2) + s 32 ROWB
   int krb[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) krb[par] = rg_off<D>(l32, 2 * par + h2);
+  for (int par = 0; par < 2; ++par) krb[par] = rg_row_base<D>(l, par);
   auto koff = [&](int kk) __attribute__((always_inline)) { return krb[kk & 1] + 256 * (kk >> 1); };
   // V^T operand by transpose reads: group g = l / 16, lane j = l % 16 reads
   // row 16 t + 4 h2 + j / 4 (+ 8 for the second read), columns
   // 32 db + 16 (g % 2) + 4 (j % 4) .. +3, at vrb[r] + 256 db + 16 t ROWB
   int vrb[2];
-  {
-    const int g = l >> 4, j = l & 15;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      vrb[r] = rg_off<D>(4 * h2 + (j >> 2) + 8 * r, 2 * (g & 1) + ((j & 3) >> 1)) + 8 * (j & 1);
-  }
+  for (int r = 0; r < 2; ++r) vrb[r] = rg_tr_base<D>(l, r);
   // direct HBM -> LDS copies: wave copy c = w + NW i fills LDS bytes
   // [1024 c, 1024 c + 1024) of a tile; lane l fills 16-byte slot 64 c + l,
   // which holds the piece rg_slot names.  Copy i of a wave reads RSTEP i
