@@ -105,11 +105,11 @@ def read_traffic():
 
 
 HBM_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/hbm_fetch -o p -- "
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/hbm_fetch -o p -- "
     "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/hbm_write -o p -- "
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/hbm_write -o p -- "
     "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
-    "python3 bench.py --hbm-summary gpurun_out/hbm_fetch gpurun_out/hbm_write",
+    "python3 bench.py --hbm-summary rocprof_out/hbm_fetch rocprof_out/hbm_write",
 ]
 
 
@@ -169,9 +169,9 @@ PIPE_PASSES = [
     "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_BF16 TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
 ]
 PIPE_COMMANDS = [
-    f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pipe{i} -o p -- "
+    f"rocprofv3 --pmc {c} --output-format csv -d rocprof_out/pipe{i} -o p -- "
     "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next" for i, c in enumerate(PIPE_PASSES)
-] + ["python3 bench.py --pipe-summary " + " ".join(f"gpurun_out/pipe{i}" for i in range(len(PIPE_PASSES)))]
+] + ["python3 bench.py --pipe-summary " + " ".join(f"rocprof_out/pipe{i}" for i in range(len(PIPE_PASSES)))]
 
 
 def pipe_summary(dirs) -> str:
@@ -237,9 +237,9 @@ def pipe_summary(dirs) -> str:
 
 STATS_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_bench_kernel_stats.md")
 STATS_COMMANDS = [
-    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_stats -o run -- "
+    "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/prof_stats -o run -- "
     "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-next",
-    "python3 bench.py --stats-summary gpurun_out/prof_stats",
+    "python3 bench.py --stats-summary rocprof_out/prof_stats",
 ]
 
 
