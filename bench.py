@@ -40,15 +40,20 @@ PEAK_HBM_GBS = 8000.0
 FWD = dict(name="fwd_b1_h32_n32768_d128_causal", B=1, H=32, N=32768, d=128, causal=True)
 BWD = dict(name="bwd_b4_h16_n4096_d128_causal", B=4, H=16, N=4096, d=128, causal=True)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_b1_h32_n32768_d128_causal_hbm_counters.json")
+BWD_COUNTERS_FILE = os.path.join(ROOT, "profiles", "bwd_kernels_b4_h16_n4096_d128_causal_hbm_counters.json")
 PIPE_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_kernels_mfma_lds_counters.md")
 # the forward kernel the long-context batch runs: 12 waves of 32 query rows
 FWD_KERNEL = "fwd_kernel<128, 12, 64, true, false>"
 FWD_KERNEL_DESC = "fwd_kernel<128,12,64,true,false> (12 waves, 384 query rows per workgroup, 64-key tiles)"
 FWD_ROWS_PER_WG, FWD_THREADS_PER_WG = 384, 768
+# the backward kernels the backward batch runs
+BWD_DQ_KERNEL = "bwd_dq_kernel<128, 8, 64, true, false>"
+BWD_MAIN_KERNEL = "bwd_main_kernel<128, true, false>"
 CSRC = os.path.join(ROOT, "io_aware_tiled_fa_amd", "csrc")
 # the forward kernel's sources (the HBM counter record is tied to these) and
 # every kernel source (the kernel-trace and pipe summaries cover all kernels)
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_layout.h")]
+BWD_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_layout.h")]
 ALL_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
                       ("fa_api.hip", "fa_bwd.hip", "fa_decode.hip", "fa_device.h", "fa_fwd.hip", "fa_kernels.h",
                        "fa_layout.h")]
@@ -106,57 +111,94 @@ def read_traffic():
 
 HBM_COMMANDS = [
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/hbm_fetch -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --no-workloads --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/hbm_write -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --no-workloads --copy-calibration",
     "python3 bench.py --hbm-summary rocprof_out/hbm_fetch rocprof_out/hbm_write",
 ]
 
 
-def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
-    """Turn the two rocprofv3 counter runs of HBM_COMMANDS into HBM bytes per
-    launch of the forward kernel on the long-context batch.  Each counter is
-    scaled by what it reads for a plain 1 GiB device copy in the same run
-    (the copy moves exactly 1 GiB each way)."""
+def bwd_algorithmic_bytes(c) -> dict:
+    """HBM bytes each backward kernel must move at least, bf16 tensors of
+    B N H d elements: the dQ kernel reads Q, dO, O, K, V and LSE and writes
+    dQ and the two float32 row terms per query row; the dK / dV kernel reads
+    Q, dO, K, V and the row terms and writes dK and dV."""
+    t = c["B"] * c["N"] * c["H"] * c["d"] * 2
+    rows = c["B"] * c["H"] * c["N"] * 4
+    return {"dq": 6 * t + rows + 2 * rows, "main": 6 * t + 2 * rows}
+
+
+def _counter_rows(d, counter):
     import csv
     import glob
 
-    fwd_threads = FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+    return rows
 
-    def read(d, counter):
-        rows = []
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
-        fwd = [float(r["Counter_Value"]) for r in rows
-               if FWD_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == fwd_threads]
-        copy = [float(r["Counter_Value"]) for r in rows if "fa::" not in r["Kernel_Name"]
-                and float(r["Counter_Value"]) > 2 ** 18]  # the 1 GiB copies (KiB units)
-        if not fwd or not copy:
-            raise SystemExit(f"{d}: no {counter} rows for the forward kernel or the copy")
-        return sum(fwd) / len(fwd), sum(copy) / len(copy), len(fwd), len(copy)
 
-    f_kib, f_copy, nf, ncf = read(fetch_dir, "FETCH_SIZE")
-    w_kib, w_copy, nw, ncw = read(write_dir, "WRITE_SIZE")
+def _per_launch(rows, kernel, threads):
+    vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"] and int(r["Grid_Size"]) == threads]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
+    """Turn the two rocprofv3 counter runs of HBM_COMMANDS into HBM bytes per
+    launch of the forward kernel on the long-context batch and of the two
+    backward kernels on the backward batch.  Each counter is scaled by what
+    it reads for a plain 1 GiB device copy in the same run (the copy moves
+    exactly 1 GiB each way)."""
+    fr, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+
+    def copy_kib(rows):  # the 1 GiB copies (KiB units)
+        vals = [float(r["Counter_Value"]) for r in rows
+                if "fa::" not in r["Kernel_Name"] and float(r["Counter_Value"]) > 2 ** 18]
+        if not vals:
+            raise SystemExit("no counter rows for the 1 GiB calibration copy")
+        return sum(vals) / len(vals), len(vals)
+
+    f_copy, ncf = copy_kib(fr)
+    w_copy, ncw = copy_kib(wr)
     gib_kib = 2.0 ** 20
     f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
-    rd, wr = f_kib * f_scale * 1024, w_kib * w_scale * 1024
-    return {
-        "kernel": FWD_KERNEL_DESC,
-        "workload": FWD["name"],
-        "kernel_source_hash": kernel_source_hash(),
-        "fetch_kib_per_launch_raw": round(f_kib, 1),
-        "write_kib_per_launch_raw": round(w_kib, 1),
-        "copy_1gib_fetch_kib_raw": round(f_copy, 1),
-        "copy_1gib_write_kib_raw": round(w_copy, 1),
-        "fetch_scale": round(f_scale, 4),
-        "write_scale": round(w_scale, 4),
-        "hbm_read_bytes_per_launch": round(rd),
-        "hbm_write_bytes_per_launch": round(wr),
-        "hbm_bytes_per_launch": round(rd + wr),
-        "algorithmic_bytes_per_launch": fwd_algorithmic_bytes(FWD),
-        "launches": {"fetch": nf, "write": nw, "copy_fetch": ncf, "copy_write": ncw},
-        "commands": HBM_COMMANDS,
-    }
+    bwd_alg = bwd_algorithmic_bytes(BWD)
+    kernels = [
+        ("fwd", FWD_KERNEL, FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG,
+         FWD_KERNEL_DESC, FWD["name"], fwd_algorithmic_bytes(FWD)),
+        ("bwd_dq", BWD_DQ_KERNEL, BWD["B"] * BWD["H"] * (BWD["N"] // 256) * 512,
+         "bwd_dq_kernel<128,8,64,true,false> (dQ and the row terms; 8 waves, 256 query rows per workgroup)",
+         BWD["name"], bwd_alg["dq"]),
+        ("bwd_main", BWD_MAIN_KERNEL, BWD["B"] * BWD["H"] * (BWD["N"] // 128) * 512,
+         "bwd_main_kernel<128,true,false> (dK and dV; 8 waves, 128 keys per workgroup)", BWD["name"],
+         bwd_alg["main"]),
+    ]
+    recs = {}
+    for key, kname, threads, desc, workload, alg in kernels:
+        f_kib, nf = _per_launch(fr, kname, threads)
+        w_kib, nw = _per_launch(wr, kname, threads)
+        if f_kib is None or w_kib is None:
+            raise SystemExit(f"no FETCH_SIZE / WRITE_SIZE rows for {kname} at {threads} threads")
+        rd, wrb = f_kib * f_scale * 1024, w_kib * w_scale * 1024
+        recs[key] = {
+            "kernel": desc,
+            "workload": workload,
+            "fetch_kib_per_launch_raw": round(f_kib, 1),
+            "write_kib_per_launch_raw": round(w_kib, 1),
+            "hbm_read_bytes_per_launch": round(rd),
+            "hbm_write_bytes_per_launch": round(wrb),
+            "hbm_bytes_per_launch": round(rd + wrb),
+            "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round((rd + wrb) / alg, 3),
+            "launches": {"fetch": nf, "write": nw},
+        }
+    calib = {"copy_1gib_fetch_kib_raw": round(f_copy, 1), "copy_1gib_write_kib_raw": round(w_copy, 1),
+             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+             "copy_launches": {"fetch": ncf, "write": ncw}}
+    fwd = dict(recs["fwd"], kernel_source_hash=kernel_source_hash(), **calib, commands=HBM_COMMANDS)
+    bwd = {"kernel_source_hash": kernel_source_hash(BWD_KERNEL_SOURCES), "dq": recs["bwd_dq"],
+           "main": recs["bwd_main"], **calib, "commands": HBM_COMMANDS}
+    return {"fwd": fwd, "bwd": bwd}
 
 
 # Pipe-utilisation counters of the kernels of one step: three rocprofv3
@@ -238,7 +280,7 @@ def pipe_summary(dirs) -> str:
 STATS_FILE = os.path.join(ROOT, "profiles", "fwd_bwd_bench_kernel_stats.md")
 STATS_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/prof_stats -o run -- "
-    "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-next",
+    "python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline",
     "python3 bench.py --stats-summary rocprof_out/prof_stats",
 ]
 
@@ -327,8 +369,19 @@ def cpu_baseline(fwd_inp, bwd_inp, budget_s: float = 20.0):
                    f"head(s) of the B=4 H=16 N=4096 d=128 causal batch ({t_b:.1f} s); "
                    f"useful-flop convention as the GPU value"),
         "seconds": round(total, 2),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (else the platform's)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main(argv=None):
@@ -338,6 +391,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the extension configurations")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the d = 64 and peaked N = 8192 forward workloads")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
@@ -353,10 +408,17 @@ def main(argv=None):
         table = stats_summary(args.stats_summary)
         with open(STATS_FILE, "w") as f:
             f.write("# rocprofv3 kernel summary\n\n"
-                    "Workloads: fa_fwd on B=1 H=32 N=32768 d=128 causal (the fwd_kernel launch of 2752 "
-                    "workgroups of 768 threads; the smaller fwd_kernel launch is the setup forward of the "
-                    "backward batch) and fa_bwd on B=4 H=16 N=4096 d=128 causal (bwd_dq_kernel = dQ "
-                    "and the row terms, then bwd_main_kernel = dK/dV).\n\n"
+                    "Workloads: fa_fwd on B=1 H=32 N=32768 d=128 causal (the fwd_kernel<128, 12, ...> "
+                    "launch of 2752 workgroups of 768 threads; the fwd_kernel<128, 8, ...> launch of 1024 "
+                    "workgroups is the setup forward of the backward batch) and fa_bwd on B=4 H=16 N=4096 "
+                    "d=128 causal (bwd_dq_kernel = dQ and the row terms, then bwd_main_kernel = dK/dV); "
+                    "then the other forward workloads (B=4 H=16 N=2048 d=64: fwd_kernel<64, 4, ...> of "
+                    "1024 workgroups; B=2 H=32 N=8192 d=128 causal peaked: fwd_kernel<128, 12, ...> of "
+                    "1408 workgroups) and the extension configurations of the bench line's `next` "
+                    "(cross attention, grouped K/V heads forward and backward, a 4096-key window, split-KV "
+                    "decoding: decode_kernel and decode_combine_kernel, and the general forward on the "
+                    "decode shape); the `Cijk`/library rows are the same-board GEMM of `context_gemm`."
+                    "\n\n"
                     f"Kernel sources hash (every file under csrc/): `{kernel_source_hash(ALL_KERNEL_SOURCES)}`"
                     "\n\nCommands (repo root, MI355X, ROCm 7.2):"
                     "\n\n```\n" + "\n".join(STATS_COMMANDS) + "\n```\n\n" + table + "\n")
@@ -380,9 +442,10 @@ def main(argv=None):
 
     if args.hbm_summary:
         rec = hbm_summary(*args.hbm_summary)
-        with open(COUNTERS_FILE, "w") as f:
-            json.dump(rec, f, indent=1)
-            f.write("\n")
+        for path, part in ((COUNTERS_FILE, rec["fwd"]), (BWD_COUNTERS_FILE, rec["bwd"])):
+            with open(path, "w") as f:
+                json.dump(part, f, indent=1)
+                f.write("\n")
         print(json.dumps(rec))
         return 0
 
@@ -509,6 +572,9 @@ def main(argv=None):
         "cpu_baseline": None,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_workloads:
+        print("# the other forward workloads", file=sys.stderr, flush=True)
+        rec["workloads"] = measure_workloads(binding, torch, dev)
     if not args.no_next:
         print("# extension configurations", file=sys.stderr, flush=True)
         rec["next"] = measure_next(binding, torch, dev)
@@ -545,79 +611,158 @@ def library_gemm_rate(torch, dev, n: int = 8192, reps: int = 150) -> dict:
             "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def measure_next(binding, torch, dev, reps: int = 7) -> dict:
-    """One configuration per extension, median of ``reps`` timed launches
-    after one untimed launch; inputs seeded N(0,1) bf16 made on the GPU."""
+def back_to_back_ms(torch, call, reps: int = 10, batches: int = 5) -> dict:
+    """Kernel time of ``call`` (a raw C-ABI launch with its arguments already
+    marshalled): ``batches`` runs of ``reps`` launches back to back between
+    two events on the current stream, after one untimed launch; the median,
+    min and max over the batches of the time per launch.  No host-side
+    validation or synchronisation sits inside a timed batch."""
+    call()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    return {"ms_median": round(statistics.median(per), 4), "ms_min": round(min(per), 4),
+            "ms_max": round(max(per), 4), "launches": reps * batches}
+
+
+def raw_forward(lib, torch, q, k, v, o, lse, causal, window=0, scale=None):
+    """A zero-argument launcher of fa_fwd / fa_fwd_qk / fa_fwd_ex (the
+    narrowest that covers the shapes), arguments marshalled once."""
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = torch.cuda.current_stream().cuda_stream
+    p = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if Hkv == H and window == 0 and Nq == Nk:
+        args, fn = p + (B, H, Nq, d, scale, int(causal), st), lib.fa_fwd
+    elif Hkv == H and window == 0:
+        args, fn = p + (B, H, Nq, Nk, d, scale, int(causal), st), lib.fa_fwd_qk
+    else:
+        args, fn = p + (B, H, Hkv, Nq, Nk, d, scale, int(causal), int(window), st), lib.fa_fwd_ex
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"forward launch failed: {lib.fa_status_string(rc).decode()}")
+    return call
+
+
+def measure_workloads(binding, torch, dev) -> dict:
+    """The two other d = 128 / d = 64 forward workloads at full size, timed
+    back to back through the C ABI, each against its own roofline: the
+    non-causal d = 64 batch (matrix-core bound with the softmax's VALU work
+    close behind: at d = 64 a score costs half the matrix work of d = 128
+    for the same exponential) and the peaked causal N = 8192 batch."""
+    from io_aware_tiled_fa_amd.inputs import make_workload
+
+    lib = binding.load_library()
+    out = {}
+    for name, causal in (("fwd_b4_h16_n2048_d64", False), ("fwd_b2_h32_n8192_d128_causal_peaked", True)):
+        inp = make_workload(name)
+        q, k, v = (device_tensor(getattr(inp, n + "_bits"), dev) for n in ("q", "k", "v"))
+        B, N, H, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        t = back_to_back_ms(torch, raw_forward(lib, torch, q, k, v, o, lse, causal), reps=20 if N < 4096 else 5)
+        cfg = dict(B=B, H=H, N=N, d=d, causal=causal)
+        fl = fwd_flops(cfg)
+        tf = fl / (t["ms_median"] * 1e-3) / 1e12
+        byts = fwd_algorithmic_bytes(cfg)
+        out[name] = dict(t, useful_tflop=round(fl / 1e12, 4), tflops=round(tf, 2), bound="mfma",
+                         frac_peak=round(tf / PEAK_BF16_TFLOPS, 4), algorithmic_bytes=byts,
+                         hbm_gbs_algorithmic=round(byts / (t["ms_median"] * 1e-3) / 1e9, 1))
+        del q, k, v, o, lse, inp
+    return out
+
+
+def measure_next(binding, torch, dev) -> dict:
+    """One configuration per extension, timed back to back through the C ABI
+    (back_to_back_ms); inputs seeded N(0,1) bf16 made on the GPU."""
     g = torch.Generator(device=dev)
     g.manual_seed(0)
+    lib = binding.load_library()
 
     def rnd(*shape):
         return torch.randn(*shape, device=dev, dtype=torch.bfloat16, generator=g)
 
-    def timed(call):
-        call()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            call()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return statistics.median(ts)
-
     out = {}
 
-    def mfma_entry(name, desc, flops, ms):
-        tf = flops / (ms * 1e-3) / 1e12
-        out[name] = {"config": desc, "ms_median": round(ms, 4), "tflops": round(tf, 2),
-                     "bound": "mfma", "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    def mfma_entry(name, desc, flops, t):
+        tf = flops / (t["ms_median"] * 1e-3) / 1e12
+        out[name] = dict(t, config=desc, tflops=round(tf, 2), bound="mfma", frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+
+    def empty_out(q):
+        return torch.empty_like(q), torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=dev)
 
     # cross attention: 4096 queries at the end of a 16384-key context
     B, H, Nq, Nk, d = 1, 32, 4096, 16384, 128
     q, k, v = rnd(B, Nq, H, d), rnd(B, Nk, H, d), rnd(B, Nk, H, d)
+    o, lse = empty_out(q)
     fl = 4.0 * B * H * d * visible_pairs(Nq, Nk, True)
     mfma_entry("fwd_cross_b1_h32_nq4096_nk16384_d128_causal", "fa_fwd_qk", fl,
-               timed(lambda: binding.forward(q, k, v, causal=True)))
-    del q, k, v
+               back_to_back_ms(torch, raw_forward(lib, torch, q, k, v, o, lse, True)))
+    del q, k, v, o, lse
 
     # grouped K/V heads, forward and backward
     B, H, Hkv, N, d = 2, 32, 8, 8192, 128
     q, do = rnd(B, N, H, d), rnd(B, N, H, d)
     k, v = rnd(B, N, Hkv, d), rnd(B, N, Hkv, d)
+    o, lse = empty_out(q)
     fl = 4.0 * B * H * d * visible_pairs(N, N, True)
     mfma_entry("fwd_gqa_b2_h32_hkv8_n8192_d128_causal", "fa_fwd_ex", fl,
-               timed(lambda: binding.forward(q, k, v, causal=True)))
-    o, lse = binding.forward(q, k, v, causal=True)
-    ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
-    mfma_entry("bwd_gqa_b2_h32_hkv8_n8192_d128_causal", "fa_bwd_ex", 2.5 * fl,
-               timed(lambda: binding.backward(q, k, v, o, lse, do, causal=True, workspace=ws)))
-    del q, k, v, do, o, lse, ws
+               back_to_back_ms(torch, raw_forward(lib, torch, q, k, v, o, lse, True)))
+    ws_bytes = binding.bwd_workspace_size(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = torch.cuda.current_stream().cuda_stream
+    bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+             dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, N, d, 1.0 / math.sqrt(d), 1, 0, ws.data_ptr(), ws_bytes, st)
+
+    def bwd_call():
+        rc = lib.fa_bwd_ex(*bargs)
+        if rc != 0:
+            raise RuntimeError(lib.fa_status_string(rc).decode())
+    mfma_entry("bwd_gqa_b2_h32_hkv8_n8192_d128_causal", "fa_bwd_ex", 2.5 * fl, back_to_back_ms(torch, bwd_call, reps=5))
+    del q, k, v, do, o, lse, ws, dq, dk, dv
 
     # sliding window of 4096 keys over a 32768-token sequence
     B, H, N, d, W = 1, 32, 32768, 128, 4096
     q, k, v = rnd(B, N, H, d), rnd(B, N, H, d), rnd(B, N, H, d)
+    o, lse = empty_out(q)
     fl = 4.0 * B * H * d * visible_pairs(N, N, True, W)
     mfma_entry("fwd_window4096_b1_h32_n32768_d128_causal", "fa_fwd_ex", fl,
-               timed(lambda: binding.forward(q, k, v, causal=True, window=W)))
-    del q, k, v
+               back_to_back_ms(torch, raw_forward(lib, torch, q, k, v, o, lse, True, window=W), reps=5))
+    del q, k, v, o, lse
 
     # split-KV decoding: one new token per sequence against a 32768-token cache
     B, H, Hkv, Nq, Nk, d = 8, 32, 8, 1, 32768, 128
     q, k, v = rnd(B, Nq, H, d), rnd(B, Nk, Hkv, d), rnd(B, Nk, Hkv, d)
-    need = binding.load_library().fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, 1, 0, 0)
+    need = lib.fa_decode_workspace_size(B, H, Hkv, Nq, Nk, d, 1, 0, 0)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
-    ms = timed(lambda: binding.decode(q, k, v, causal=True, out=o, lse=lse, workspace=ws))
+    o, lse = empty_out(q)
+    st = torch.cuda.current_stream().cuda_stream
+    dargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk, d,
+             1.0 / math.sqrt(d), 1, 0, 0, ws.data_ptr(), ws.numel(), st)
+
+    def dec_call():
+        rc = lib.fa_fwd_decode(*dargs)
+        if rc != 0:
+            raise RuntimeError(lib.fa_status_string(rc).decode())
+    t = back_to_back_ms(torch, dec_call, reps=50)
     byts = 2 * B * Nk * Hkv * d * 2 + 2 * B * Nq * H * d * 2 + B * H * Nq * 4
-    gbs = byts / (ms * 1e-3) / 1e9
-    out["decode_b8_h32_hkv8_nq1_nk32768_d128"] = {
-        "config": "fa_fwd_decode", "ms_median": round(ms, 4), "gbs": round(gbs, 1), "bound": "hbm",
-        "frac_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": byts}
-    ms_f = timed(lambda: binding.forward(q, k, v, causal=True, out=o, lse=lse))
-    out["decode_b8_h32_hkv8_nq1_nk32768_d128"]["general_forward_ms"] = round(ms_f, 4)
+    gbs = byts / (t["ms_median"] * 1e-3) / 1e9
+    out["decode_b8_h32_hkv8_nq1_nk32768_d128"] = dict(
+        t, config="fa_fwd_decode", gbs=round(gbs, 1), bound="hbm", frac_peak=round(gbs / PEAK_HBM_GBS, 4),
+        algorithmic_bytes=byts)
+    out["decode_b8_h32_hkv8_nq1_nk32768_d128"]["general_forward_ms"] = back_to_back_ms(
+        torch, raw_forward(lib, torch, q, k, v, o, lse, True), reps=20)["ms_median"]
     return out
 
 

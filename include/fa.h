@@ -38,7 +38,9 @@
  *  - Base pointers must be 16-byte aligned.  Outputs must not alias inputs.
  *  - d must be 64 or 128.  B, H, H_kv, N_q, N_k >= 1 (any length: the
  *    kernels mask ragged tiles), H a multiple of H_kv, and each tensor must
- *    have fewer than 2^31 elements.
+ *    have fewer than 2^31 elements; so must (N_q + 128) * H * d and
+ *    (N_k + 128) * H_kv * d (one batch's rows plus the zero-filled rows a
+ *    tile copy may run past the end), else FA_ERR_SHAPE.
  *  - scale is any finite float (0 allowed; negative allowed).
  *  - causal: 0 = every key visible; 1 = key j visible to query i iff
  *    j <= i + (N_k - N_q), i.e. the keys are aligned to the end of the

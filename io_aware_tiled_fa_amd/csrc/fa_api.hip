@@ -27,11 +27,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // Sizes: B, H, H_kv, N_q, N_k >= 1, H a multiple of H_kv, d in {64, 128},
 // and every tensor under 2^31 elements (the kernels index in 32-bit element
-// offsets within a tensor).
+// offsets within a tensor).  The tile copies address one batch's rows of a
+// head in 32-bit byte offsets that run up to 128 rows past its last row
+// (those read zero), so (N + 128) rows of a batch must also stay under 2^31
+// elements.
 fa_status check_shape(int B, int H, int Hkv, int Nq, int Nk, int d) {
   if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if ((long long)B * Nq * H * d > 0x7FFFFFFFLL || (long long)B * Nk * Hkv * d > 0x7FFFFFFFLL) return FA_ERR_SHAPE;
+  const long long lim = 0x7FFFFFFFLL;
+  if ((long long)B * Nq * H * d > lim || (long long)B * Nk * Hkv * d > lim) return FA_ERR_SHAPE;
+  if (((long long)Nq + 128) * H * d > lim || ((long long)Nk + 128) * Hkv * d > lim) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -77,6 +82,62 @@ int decode_splits(int B, int Hkv, int d, int nst, int requested) {
   return want < 1 ? 1 : (int)want;
 }
 
+// Arguments of the backward other than its workspace: pointers, sizes,
+// alignment, scale and flags, and no output overlapping an input or another
+// output.
+fa_status bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int d,
+                    float scale, int causal, int window) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  const void* all[] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : all)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_ARG;
+  const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * Hkv * d * 2, lb = (size_t)B * H * Nq * 4;
+  const void* ins[6] = {q, k, v, o, dO, lse};
+  const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
+  void* outs[3] = {dq, dk, dv};
+  const size_t outsz[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
+  }
+  return FA_OK;
+}
+
+// Launch the backward kernels with `drow` (2 B H N_q floats) for the row terms.
+fa_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, int window, float* drow, void* stream) {
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.lse = lse;
+  a.dO = static_cast<const __bf16*>(dO);
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.drow = drow;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.G = H / Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  const bool band = band_of(Nq, Nk, causal, window, a.wl, a.wr);
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_bwd(a, d, band, window > 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,7 +146,7 @@ const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H, H_kv, N_q and N_k must be positive, H a multiple of H_kv, and every tensor must have fewer than 2^31 elements";
+    case FA_ERR_SHAPE: return "B, H, H_kv, N_q and N_k must be positive, H a multiple of H_kv, every tensor must have fewer than 2^31 elements, and so must (N_q + 128) H d and (N_k + 128) H_kv d";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_SEQLEN: return "sequence length not supported";
     case FA_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
@@ -219,51 +280,18 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, Hkv, Nq, Nk, d);
+  fa_status st = bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal, window);
   if (st != FA_OK) return st;
-  const void* all[] = {q, k, v, o, lse, dO, dq, dk, dv};
-  for (const void* p : all)
-    if (!aligned16(p)) return FA_ERR_ALIGN;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_ARG;
   const size_t need = fa_bwd_workspace_size(B, H, Nq, d);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FA_ERR_WORKSPACE;
   const size_t qb = (size_t)B * Nq * H * d * 2, kb = (size_t)B * Nk * Hkv * d * 2, lb = (size_t)B * H * Nq * 4;
-  const void* ins[6] = {q, k, v, o, dO, lse};
-  const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
-  void* outs[4] = {dq, dk, dv, workspace};
-  const size_t outsz[4] = {qb, kb, kb, need};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ARG;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ARG;
-  }
-
-  fa::BwdArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
-  a.o = static_cast<const __bf16*>(o);
-  a.lse = lse;
-  a.dO = static_cast<const __bf16*>(dO);
-  a.dq = static_cast<__bf16*>(dq);
-  a.dk = static_cast<__bf16*>(dk);
-  a.dv = static_cast<__bf16*>(dv);
-  a.drow = static_cast<float*>(workspace);
-  a.B = B;
-  a.H = H;
-  a.Hkv = Hkv;
-  a.G = H / Hkv;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  const bool band = band_of(Nq, Nk, causal, window, a.wl, a.wr);
-  a.scale = scale;
-  a.c = scale * 1.4426950408889634f;
-  const hipError_t e = fa::launch_bwd(a, d, band, window > 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const void* others[9] = {q, k, v, o, dO, lse, dq, dk, dv};
+  const size_t othersz[9] = {qb, kb, kb, qb, qb, lb, qb, kb, kb};
+  for (int j = 0; j < 9; ++j)
+    if (overlaps(workspace, need, others[j], othersz[j])) return FA_ERR_ARG;
+  return bwd_launch(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal, window,
+                    static_cast<float*>(workspace), stream);
 }
 
 fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,

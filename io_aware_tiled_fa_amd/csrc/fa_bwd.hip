@@ -152,7 +152,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // their LDS writes wait for): copy i of consumer wave w - 4 is 1 KiB slot
   // w - 4 + 4 i of the pair (Q tile slots first, then dO)
   // (byte offsets from the tile's first row, one unsigned 32-bit value per
-  // copy, into buffer resources over this head's Q and dO rows)
+  // copy, into buffer resources over this head's Q and dO rows based at
+  // the block's first row)
   uint32_t qgoff[QLPW];
 #pragma unroll
   for (int i = 0; i < QLPW; ++i) {
@@ -182,29 +183,34 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // over that head's Q and dO rows and the offset of its row terms, rebuilt
   // only when the walk moves on to the next head.
   int hq_next = hk * G, qb_next = 0;
-  buf_rsrc qrs, grs;
+  const __bf16* qhead = nullptr;
+  const __bf16* ghead = nullptr;
+  uint32_t head_bytes = 0;
   size_t rt_head = 0;
   auto set_head = [&]() __attribute__((always_inline)) {
     // query head hq_next's rows 0 .. N_q - 1 at a stride of H d, the last
-    // ending H d - hq d elements before the end of the batch's span; under
-    // 2^32 bytes since B N_q H d < 2^31 (rows past N_q read zero)
-    const uint32_t head_bytes = (uint32_t)(((size_t)a.Nq * a.H - hq_next) * D * 2);
-    qrs = make_rsrc(a.q + qb_off + (size_t)hq_next * D, head_bytes);
-    grs = make_rsrc(a.dO + qb_off + (size_t)hq_next * D, head_bytes);
+    // ending H d - hq d elements before the end of the batch's span.
+    // Offsets stay under 2^32 bytes (the host requires (N_q + 128) H d <
+    // 2^31).
+    head_bytes = (uint32_t)(((size_t)a.Nq * a.H - hq_next) * D * 2);
+    qhead = a.q + qb_off + (size_t)hq_next * D;
+    ghead = a.dO + qb_off + (size_t)hq_next * D;
     rt_head = ((size_t)b * a.H + hq_next) * a.Nq;
   };
   // copies of query block qblk of the current head into Q / dO / row-term buffer I
   auto issue_q = [&](int qblk, auto I) __attribute__((always_inline)) {
     if (producer) return;
-    const uint32_t soff = (uint32_t)qblk * (uint32_t)(BR * rs * 2);
+    // (resources based at the block's first row: the per-lane offsets are
+    // all the range check sees, so rows past N_q read zero)
+    const uint32_t boff = (uint32_t)qblk * (uint32_t)(BR * rs * 2);
 #pragma unroll
     for (int i = 0; i < QLPW; ++i) {
       const int slot = (w & 3) + 4 * i;  // wave-uniform
       const int c = slot % (QTILEB / 1024);
       if (slot < QTILEB / 1024)
-        copy16_to_lds_buf(qrs, qgoff[i], soff, (lds_void*)(QT(I) + c * 1024));
+        copy16_to_lds_buf(make_rsrc_at(qhead, head_bytes, boff), qgoff[i], (lds_void*)(QT(I) + c * 1024));
       else
-        copy16_to_lds_buf(grs, qgoff[i], soff, (lds_void*)(GT(I) + c * 1024));
+        copy16_to_lds_buf(make_rsrc_at(ghead, head_bytes, boff), qgoff[i], (lds_void*)(GT(I) + c * 1024));
     }
     // the row terms are copied by a consumer wave, so the producers' writes
     // to the P^T / dS^T tiles never wait behind a copy the compiler cannot
@@ -596,16 +602,19 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     rg_slot<D>(64 * (w + NW * i) + l, row, piece);
     goff[i] = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
-  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);  // (rows past N_k read zero)
-  const buf_rsrc krs = make_rsrc(kbase, head_bytes);
-  const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
+  // (resources based at the tile's first row: the per-lane offsets are all
+  // the range check sees, so rows past N_k read zero; offsets under 2^32
+  // bytes, as in the forward kernel)
+  const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
+    const uint32_t toff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
+    const buf_rsrc krs = make_rsrc_at(kbase, head_bytes, toff);
+    const buf_rsrc vrs = make_rsrc_at(vbase, head_bytes, toff);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      copy16_to_lds_buf(krs, goff[i], soff, (lds_void*)(kdst + c * 1024));
-      copy16_to_lds_buf(vrs, goff[i], soff, (lds_void*)(vdst + c * 1024));
+      copy16_to_lds_buf(krs, goff[i], (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(vrs, goff[i], (lds_void*)(vdst + c * 1024));
     }
   };
 

@@ -107,19 +107,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecArgs a) {
     goff = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
   // K and V of this (batch, key head): rows 0 .. N_k - 1 at a stride of
-  // H_kv d, under 2^32 bytes since B N_k H_kv d < 2^31 (rows past N_k read zero)
+  // H_kv d.  Each copy rebases its resource at the rows it starts from, so
+  // its per-lane offset goff is all the range check sees: rows past N_k read
+  // zero.  Offsets stay under 2^32 bytes (the host requires
+  // (N_k + 128) H_kv d < 2^31).
   const size_t kv_off = (size_t)b * a.Nk * rk + (size_t)hk * D;
   const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);
-  const buf_rsrc krs = make_rsrc(a.k + kv_off, head_bytes);
-  const buf_rsrc vrs = make_rsrc(a.v + kv_off, head_bytes);
+  const __bf16* kbase = a.k + kv_off;
+  const __bf16* vbase = a.v + kv_off;
   auto issue_stage = [&](int st, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)st * (uint32_t)(BS * rk * 2);
+    const uint32_t toff = (uint32_t)st * (uint32_t)(BS * rk * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
-      const uint32_t so = soff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
-      copy16_to_lds_buf(krs, goff, so, (lds_void*)(kdst + c * 1024));
-      copy16_to_lds_buf(vrs, goff, so, (lds_void*)(vdst + c * 1024));
+      const uint32_t off = toff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
+      copy16_to_lds_buf(make_rsrc_at(kbase, head_bytes, off), goff, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(make_rsrc_at(vbase, head_bytes, off), goff, (lds_void*)(vdst + c * 1024));
     }
   };
 

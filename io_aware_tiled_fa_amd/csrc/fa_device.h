@@ -69,18 +69,41 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Buffer resource over `bytes` bytes from `base` (raw, untyped: the fourth
-// descriptor word of the gfx9 family).  Accesses past `bytes` read zero.
+// descriptor word of the gfx9 family).  A load whose per-lane offset is at or
+// past `bytes` reads zero and touches no memory.
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Buffer resource over the bytes [off, bytes) of the span at `base`, based
+// at base + off: an empty one (every access reads zero) when off >= bytes.
+// All arguments are wave-uniform, so this is a few scalar instructions; the
+// kernels rebase their resources at each tile this way, which keeps a
+// tile's per-lane offsets small and range-checked.
+__device__ __forceinline__ buf_rsrc make_rsrc_at(const void* base, uint32_t bytes, uint32_t off) {
+  // Both words are read back into scalar registers: the saturating
+  // subtraction has no scalar instruction, and a 64-bit address product may
+  // be formed by vector instructions; a resource the compiler finds in
+  // vector registers is treated as per-lane, and every access through it
+  // becomes a loop over the lanes' values.
+  const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(base) + off);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+  const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(off < bytes ? bytes - off : 0u));
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), left);
+}
+
 // 16-byte asynchronous copy global -> LDS through a buffer resource: lane l
-// writes bytes [lds + 16 l, lds + 16 l + 16) from byte voff + soff of the
-// buffer (voff per lane, soff wave-uniform).  Unlike copy16_to_lds this
-// needs one VGPR per copy instead of a 64-bit address.
-__device__ __forceinline__ void copy16_to_lds_buf(buf_rsrc r, uint32_t voff, uint32_t soff, lds_void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+// writes bytes [lds + 16 l, lds + 16 l + 16) from byte `voff` of the buffer.
+// The range check of a raw buffer access compares only the per-lane offset
+// (plus the instruction's immediate) with the resource's size; the scalar
+// offset operand is added after the check.  So the whole offset goes into
+// `voff` and the scalar operand is always 0: a row past the end of the
+// buffer then reads zero instead of whatever memory follows it.  Unlike a
+// flat copy this needs one VGPR per copy instead of a 64-bit address.
+__device__ __forceinline__ void copy16_to_lds_buf(buf_rsrc r, uint32_t voff, lds_void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
 }
 
 // wait until every outstanding vector-memory load of this wave has landed

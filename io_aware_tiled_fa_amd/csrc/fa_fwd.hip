@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
   // which holds the piece rg_slot names.  Copy i of a wave reads RSTEP i
   // rows further down than its copy 0, and RSTEP is a multiple of 16, where
   // the layout repeats, so one per-lane byte offset (from the tile's first
-  // row) serves every copy, the rest going into the scalar offset.
+  // row) serves every copy, each copy's resource based at its first row.
   constexpr int RSTEP = 64 * NW / NCH;
   static_assert(RSTEP % 16 == 0, "copies of a wave must keep the row-group layout");
   uint32_t goff;
@@ -155,22 +155,23 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
     rg_slot<D>(64 * w + l, row, piece);
     goff = (uint32_t)(row * (int)rk + piece * 8) * 2u;
   }
-  // K and V of this (batch, key head) as buffer resources: rows 0 .. N_k - 1
-  // at a stride of H_kv d elements, the last ending H_kv d - hk d elements
-  // before the end of the head's span; under 2^32 bytes since B N_k H_kv d
-  // < 2^31 (rows past N_k read zero)
+  // K and V of this (batch, key head) through buffer resources: rows
+  // 0 .. N_k - 1 at a stride of H_kv d elements, the last ending H_kv d - hk d
+  // elements before the end of the head's span.  Each copy rebases its
+  // resource at the rows it starts from (scalar work), so its per-lane
+  // offset goff is all the range check sees: rows past N_k read zero.
+  // Offsets stay under 2^32 bytes (the host requires (N_k + 128) H_kv d
+  // < 2^31).
   const uint32_t head_bytes = (uint32_t)(((size_t)a.Nk * a.Hkv - hk) * D * 2);
-  const buf_rsrc krs = make_rsrc(kbase, head_bytes);
-  const buf_rsrc vrs = make_rsrc(vbase, head_bytes);
   auto issue_tile = [&](int kt, lds_char* kdst, lds_char* vdst) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
+    const uint32_t toff = (uint32_t)kt * (uint32_t)(BC * rk * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = w + NW * i;
       if (LOADS % NW != 0 && c >= LOADS) break;  // (wave-uniform)
-      const uint32_t so = soff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
-      copy16_to_lds_buf(krs, goff, so, (lds_void*)(kdst + c * 1024));
-      copy16_to_lds_buf(vrs, goff, so, (lds_void*)(vdst + c * 1024));
+      const uint32_t off = toff + (uint32_t)(i * RSTEP) * (uint32_t)(rk * 2);
+      copy16_to_lds_buf(make_rsrc_at(kbase, head_bytes, off), goff, (lds_void*)(kdst + c * 1024));
+      copy16_to_lds_buf(make_rsrc_at(vbase, head_bytes, off), goff, (lds_void*)(vdst + c * 1024));
     }
   };
 

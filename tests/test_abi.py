@@ -125,6 +125,12 @@ def test_cross_shape_validation(lib):
     assert fwd_qk(lib, Nk=-5) == -2
     assert fwd_qk(lib, Nq=1, Nk=2 ** 31 - 1, H=2, d=128) == -2   # K holds > 2^31 elements
     assert fwd_qk(lib, Nq=77, Nk=300, scale=float("nan")) == -7
+    # the tile copies address up to 128 rows past a head's last row in 32-bit
+    # byte offsets: (N_k + 128) H d must stay under 2^31 as well
+    assert fwd_qk(lib, Nq=1, Nk=2 ** 24 - 64, d=128) == -2           # K itself fits, the margin does not
+    assert fwd_qk(lib, Nq=1, Nk=2 ** 24 - 128, d=128) == -2
+    assert fwd_qk(lib, Nq=1, Nk=2 ** 24 - 129, d=128, scale=float("nan")) == -7
+    assert fwd_qk(lib, Nq=2 ** 24 - 64, Nk=1, d=128) == -2           # the same for Q
     assert fwd_qk(lib, Nq=300, Nk=77, d=80) == -3
     assert fwd_qk(lib, o=P[1]) == -9                               # output aliases K
     assert bwd_qk(lib, Nq=0) == -2
@@ -236,15 +242,64 @@ def test_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(1, 3, 64, 64) == r256(3 * 64 * 4 * 2)
 
 
-def test_binding_refuses_cpu_tensors():
+def test_binding_input_checks():
+    """The binding's checks of the tensors the C ABI cannot see; every
+    other check passes first, so the last error is the device."""
     import torch
 
     from io_aware_tiled_fa_amd import binding
 
-    q = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError, match="GPU"):
-        binding.validate_attention_inputs(q, q, q)
-    with pytest.raises(TypeError):
-        binding.validate_attention_inputs(q.float(), q, q)
-    with pytest.raises(ValueError, match="4 dimensions"):
-        binding.validate_attention_inputs(q[0], q, q)
+    q = torch.zeros(2, 64, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(2, 80, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        binding.check_inputs(q, kv, kv)              # valid shapes, but on the CPU
+    with pytest.raises(TypeError, match="dtype"):
+        binding.check_inputs(q.float(), kv, kv)
+    with pytest.raises(ValueError, match="dims"):
+        binding.check_inputs(q[0], kv, kv)
+    with pytest.raises(TypeError, match="not a torch.Tensor"):
+        binding.check_inputs(q, kv.float().numpy(), kv)
+    with pytest.raises(ValueError, match="share batch"):
+        binding.check_inputs(q, kv[:1], kv[:1])      # batch differs
+    with pytest.raises(ValueError, match="share batch"):
+        binding.check_inputs(q, kv[..., :32], kv[..., :32])   # head_dim differs
+    with pytest.raises(ValueError, match="share batch"):
+        binding.check_inputs(q, torch.zeros(2, 80, 3, 64, dtype=torch.bfloat16), kv)  # 4 heads over 3
+    with pytest.raises(ValueError, match="shape"):
+        binding.check_inputs(q, kv, kv[:, :79])      # K and V lengths differ
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.check_inputs(q, kv, kv.transpose(1, 2).contiguous().transpose(1, 2))
+
+
+def test_binding_output_checks():
+    """Caller-supplied outputs and workspaces are checked against the call's
+    sizes, dtype, device and contiguity before any pointer reaches the C ABI."""
+    import torch
+
+    from io_aware_tiled_fa_amd import binding
+
+    q = torch.zeros(2, 64, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(2, 80, 2, 64, dtype=torch.bfloat16)
+    shp = binding.AttentionShape(q, kv)
+    cpu = q.device
+    o, lse = binding._outputs(shp, cpu)
+    assert tuple(o.shape) == (2, 64, 4, 64) and o.dtype == torch.bfloat16
+    assert tuple(lse.shape) == (2, 4, 64) and lse.dtype == torch.float32
+    with pytest.raises(ValueError, match="shape"):
+        binding._outputs(shp, cpu, o=torch.zeros(2, 64, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        binding._outputs(shp, cpu, lse=torch.zeros(2, 4, 63))
+    with pytest.raises(TypeError, match="dtype"):
+        binding._outputs(shp, cpu, o=torch.zeros(2, 64, 4, 64))
+    with pytest.raises(TypeError, match="dtype"):
+        binding._outputs(shp, cpu, lse=torch.zeros(2, 4, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        binding._outputs(shp, cpu, lse=torch.zeros(2, 64, 4).transpose(1, 2))
+    with pytest.raises(ValueError, match="is on"):
+        binding._outputs(shp, torch.device("meta"), o=o)
+    with pytest.raises(ValueError, match="needs 512"):
+        binding._workspace(torch.zeros(100, dtype=torch.uint8), 512, cpu)
+    with pytest.raises(TypeError, match="uint8"):
+        binding._workspace(torch.zeros(512), 512, cpu)
+    assert binding._workspace(None, 0, cpu) is None
+    assert binding._workspace(None, 300, cpu).numel() == 300

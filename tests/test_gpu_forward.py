@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 from io_aware_tiled_fa_amd.inputs import make_inputs, make_workload
-from parity import (TOL_LSE, TOL_O, TOL_O_MEAN, announce, compare, forward_error_bound, sample_rows,
-                    to_device, to_numpy_f32)
+from parity import (TOL_LSE, TOL_O, TOL_O_MEAN, announce, compare, forward_error_bound,
+                    oracle_forward_by_head, to_device, to_numpy_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,18 +114,31 @@ def test_workload_fwd_b4_h16_n2048_d64(fa):
     check_fwd(fa, inp, False, 1.0 / 8.0)
 
 
+def check_workload_every_element(fa, inp, scale):
+    """Every element of O and LSE against the oracle (run head by head over
+    the host's cores; a minute or two for the long workloads)."""
+    o, lse = run_fwd(fa, inp, True, scale)
+    o_np, lse_np = to_numpy_f32(o), lse.cpu().numpy()
+    del o, lse
+    o_ref, lse_ref = oracle_forward_by_head(inp, scale, True)
+    compare("O", o_np, o_ref, TOL_O, TOL_O_MEAN)
+    compare("LSE", lse_np, lse_ref, TOL_LSE, ulp_aware=False)
+    return o_np, o_ref
+
+
+@pytest.mark.timeout(900)
 def test_workload_fwd_b2_h32_n8192_d128_causal_peaked(fa):
-    """Sampled rows (each row is exact on its own), every peaked row included."""
-    announce("fwd workload B=2 H=32 N=8192 d=128 causal peaked (sampled rows)")
+    """Every element; the peaked rows (Q x4) are also checked on their own."""
+    announce("fwd workload B=2 H=32 N=8192 d=128 causal peaked (every element)")
     inp = make_workload("fwd_b2_h32_n8192_d128_causal_peaked")
-    rng = np.random.default_rng(0)
-    rows = sample_rows(8192, 96, rng, extra=inp.peaked_rows[0, 0].tolist() + inp.peaked_rows[1, 5].tolist())
-    check_fwd(fa, inp, True, 1.0 / math.sqrt(128), rows=rows)
+    o_np, o_ref = check_workload_every_element(fa, inp, 1.0 / math.sqrt(128))
+    b_idx, h_idx, _ = np.indices(inp.peaked_rows.shape)
+    sel = (b_idx.ravel(), inp.peaked_rows.ravel(), h_idx.ravel())
+    compare("O peaked rows", o_np[sel], o_ref[sel], TOL_O, TOL_O_MEAN)
 
 
+@pytest.mark.timeout(900)
 def test_workload_fwd_b1_h32_n32768_d128_causal(fa):
-    announce("fwd workload B=1 H=32 N=32768 d=128 causal (sampled rows)")
+    announce("fwd workload B=1 H=32 N=32768 d=128 causal (every element)")
     inp = make_workload("fwd_b1_h32_n32768_d128_causal")
-    rng = np.random.default_rng(1)
-    rows = sample_rows(32768, 48, rng)
-    check_fwd(fa, inp, True, 1.0 / math.sqrt(128), rows=rows)
+    check_workload_every_element(fa, inp, 1.0 / math.sqrt(128))

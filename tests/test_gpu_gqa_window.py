@@ -91,8 +91,9 @@ def test_gqa_equals_repeated_heads(fa):
     """Grouped heads give exactly what plain multi-head attention gives on
     K and V with each head repeated over its group (the same tiles in the
     same order), and dK / dV of a shared head are the group sums of the
-    repeated heads' gradients (compared within the gradient gate: the sums
-    round differently)."""
+    repeated heads' gradients: the group sum is formed once in float32 and
+    rounded, the repeated heads' gradients are each rounded first, so the
+    two may differ by half a bf16 ulp of every term and of the sum."""
     import torch
 
     announce("gqa == repeated heads")
@@ -109,33 +110,34 @@ def test_gqa_equals_repeated_heads(fa):
     assert torch.equal(o.view(torch.int16), o_r.view(torch.int16))
     assert torch.equal(lse, lse_r)
     assert torch.equal(dq.view(torch.int16), dq_r.view(torch.int16))
+    def half_ulp(x):
+        return torch.exp2(torch.floor(torch.log2(x.abs().clamp_min(2.0 ** -126))) - 8)
+
     for name, got, rep in (("dK", dk, dk_r), ("dV", dv, dv_r)):
-        want = rep.float().view(B, N, Hkv, H // Hkv, d).sum(dim=3)
-        err = (got.float() - want).abs().max().item()
-        assert err <= 3e-2 + 2 ** -7 * want.abs().max().item(), f"{name}: {err}"
+        terms = rep.float().view(B, N, Hkv, H // Hkv, d)
+        want = terms.sum(dim=3)
+        err = (got.float() - want).abs()
+        # each term's rounding, the sum's rounding, and the float32 sum itself
+        limit = half_ulp(terms).sum(dim=3) + half_ulp(got.float()) + 1e-5 * terms.abs().sum(dim=3)
+        assert bool((err <= limit).all()), f"{name}: {(err - limit).max().item()} over the limit"
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("causal,window", [(True, 1000), (False, 700)])
 def test_window_large_grid_ragged(fa, causal, window):
     """d = 128 windowed grids of at least 1024 workgroups of 384 rows run the
-    12-wave forward kernel; N = 6000 ends ragged in its query tiles.  Sampled
-    rows (tile and window edges, the last rows, a random sample) against the
-    oracle; rows are independent, so a sampled row is exact."""
-    import numpy as np
+    12-wave forward kernel; N = 6000 ends ragged in its query tiles.  Every
+    element against the oracle."""
     import torch
 
-    import oracle
-    from parity import TOL_LSE, TOL_O, compare, sample_rows, to_numpy_f32
+    from parity import TOL_LSE, TOL_O, TOL_O_MEAN, compare, oracle_forward_by_head, to_numpy_f32
 
     N = 6000
-    announce(f"fwd window large grid B=2 H=32 N={N} d=128 causal={causal} W={window}")
+    announce(f"fwd window large grid B=2 H=32 N={N} d=128 causal={causal} W={window} (every element)")
     inp = _inputs(2, 32, 8, N, N, 128, 9100 + window, False)
     q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
     o, lse = fa.forward(q, k, v, causal=causal, window=window)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    rows = sample_rows(N, 40, rng, extra=[383, 384, window - 1, window, window + 383, N - 385])
-    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, 1.0 / math.sqrt(128), causal, rows=rows,
-                                              window=window)
-    compare("O", to_numpy_f32(o)[:, rows], o_ref, TOL_O)
-    compare("LSE", lse.cpu().numpy()[:, :, rows], lse_ref, TOL_LSE, ulp_aware=False)
+    o_ref, lse_ref = oracle_forward_by_head(inp, 1.0 / math.sqrt(128), causal, window=window)
+    compare("O", to_numpy_f32(o), o_ref, TOL_O, TOL_O_MEAN)
+    compare("LSE", lse.cpu().numpy(), lse_ref, TOL_LSE, ulp_aware=False)

@@ -110,25 +110,21 @@ def test_cross_equals_suffix_of_self(fa):
     assert torch.equal(lse_suf, lse_full[:, :, Nk - Nq:])
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("B,H,Nq,Nk", [(2, 32, 6000, 6000), (4, 32, 3000, 4500)])
 def test_forward_large_grid_ragged(fa, B, H, Nq, Nk):
     """Causal d = 128 grids of at least 1024 workgroups of 384 rows run the
     12-wave forward kernel; these end ragged in its 384-row query tiles.
-    Sampled rows (tile edges, the last rows and a random sample) against the
-    oracle; rows are independent, so a sampled row is exact."""
-    import numpy as np
+    Every element against the oracle."""
     import torch
 
-    import oracle
-    from parity import TOL_LSE, TOL_O, compare, sample_rows, to_numpy_f32
+    from parity import TOL_LSE, TOL_O, TOL_O_MEAN, compare, oracle_forward_by_head, to_numpy_f32
 
-    announce(f"fwd large grid B={B} H={H} Nq={Nq} Nk={Nk} d=128 causal")
+    announce(f"fwd large grid B={B} H={H} Nq={Nq} Nk={Nk} d=128 causal (every element)")
     inp = make_inputs(B, H, Nq, 128, N_k=Nk, seed=7700 + Nq)
     q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
     o, lse = fa.forward(q, k, v, causal=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    rows = sample_rows(Nq, 40, rng, extra=[383, 384, 767, 768, 1151, Nq - 385, Nq - 384])
-    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, 1.0 / math.sqrt(128), True, rows=rows)
-    compare("O", to_numpy_f32(o)[:, rows], o_ref, TOL_O)
-    compare("LSE", lse.cpu().numpy()[:, :, rows], lse_ref, TOL_LSE, ulp_aware=False)
+    o_ref, lse_ref = oracle_forward_by_head(inp, 1.0 / math.sqrt(128), True)
+    compare("O", to_numpy_f32(o), o_ref, TOL_O, TOL_O_MEAN)
+    compare("LSE", lse.cpu().numpy(), lse_ref, TOL_LSE, ulp_aware=False)
