@@ -77,8 +77,10 @@ typedef enum {
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required         */
   FA_ERR_SCALE = -7,      /* scale is NaN or infinite                        */
   FA_ERR_LAUNCH = -8,     /* the HIP launch reported an error                */
-  FA_ERR_ARG = -9         /* causal not 0/1, window or num_splits < 0, or an */
-                          /* output aliases an input or another output       */
+  FA_ERR_ARG = -9,        /* causal not 0/1, window or num_splits < 0, an    */
+                          /* output aliases an input or another output, or   */
+                          /* (fa_bwd_noalloc) a stream of another device     */
+  FA_ERR_SCRATCH = -10    /* fa_bwd_noalloc: B * H * N_q above 2^21 rows     */
 } fa_status;
 
 /*
@@ -196,6 +198,26 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Arguments and results
+ * are those of fa_bwd_ex without the workspace: the row terms go to a
+ * static scratch array of 16 MiB inside the library, one per GPU, held
+ * until the process ends.
+ *  - Limit: B * H * N_q <= 2^21 query rows (8 bytes of scratch per row);
+ *    larger problems return FA_ERR_SCRATCH and launch nothing.
+ *  - stream must belong to the current device (else FA_ERR_ARG).  The first
+ *    call on a device looks up that device's scratch address.
+ *  - Calls that overlap on one GPU (concurrent streams, or threads) share
+ *    the array and race; serialise them.  Nothing in it needs to start at
+ *    zero: each call writes every row term before reading it.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal, int window,
+                         void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status s);

@@ -32,10 +32,10 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 FA_STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM",
     -4: "FA_ERR_SEQLEN", -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE",
-    -7: "FA_ERR_SCALE", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_ARG",
+    -7: "FA_ERR_SCALE", -8: "FA_ERR_LAUNCH", -9: "FA_ERR_ARG", -10: "FA_ERR_SCRATCH",
 }
 EXPORTED = ("fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_fwd_decode", "fa_decode_workspace_size", "fa_bwd",
-            "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_status_string", "fa_version")
+            "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_workspace_size", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -68,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_ex.restype = i
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_decode.restype = i
     lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_decode_workspace_size.restype = sz

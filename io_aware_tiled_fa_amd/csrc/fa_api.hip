@@ -13,10 +13,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_kernels.h"
 
 namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;  // fa_bwd_noalloc: B H N_q <= 2^21 rows
+constexpr int kMaxScratchDevices = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -140,6 +145,33 @@ fa_status bwd_launch(const void* q, const void* k, const void* v, const void* o,
 
 }  // namespace
 
+// Scratch memory of fa_bwd_noalloc, for callers that cannot allocate: the
+// backward's two float32 row terms per query row live here instead of in a
+// caller's workspace.  One copy per GPU, held until the process ends; in
+// host code the name stands for the host-side shadow, so its device
+// address is looked up once per device and only that address is used.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex scratch_mutex;
+float* scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device, or nullptr.
+float* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fa_status_string(fa_status s) {
@@ -153,7 +185,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_SCALE: return "scale must be a finite float";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "causal must be 0 or 1, window and num_splits must not be negative, and outputs must not overlap inputs";
+    case FA_ERR_ARG: return "causal must be 0 or 1, window and num_splits must not be negative, outputs must not overlap inputs, and the stream must belong to the current device";
+    case FA_ERR_SCRATCH: return "fa_bwd_noalloc holds at most 2^21 query rows (B * H * N_q) in its static scratch";
   }
   return "unknown status";
 }
@@ -292,6 +325,23 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
     if (overlaps(workspace, need, others[j], othersz[j])) return FA_ERR_ARG;
   return bwd_launch(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal, window,
                     static_cast<float*>(workspace), stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                         void* stream) {
+  fa_status st = bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal, window);
+  if (st != FA_OK) return st;
+  if (fa_bwd_workspace_size(B, H, Nq, d) > kScratchBytes) return FA_ERR_SCRATCH;
+  // the scratch array of the stream's device, which must be the current one
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  if (dev != cur) return FA_ERR_ARG;
+  float* rows = scratch_of_current_device();
+  if (!rows) return FA_ERR_LAUNCH;
+  return bwd_launch(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, Nq, Nk, d, scale, causal, window, rows, stream);
 }
 
 fa_status fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_qk", "fa_fwd_ex", "fa_fwd_decode", "fa_decode_workspace_size", "fa_bwd",
-         "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
+         "fa_bwd_qk", "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_workspace_size", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = lib.fa_status_string(code)
         assert s and s != b"unknown status", code
     assert lib.fa_status_string(-99) == b"unknown status"
@@ -303,3 +303,21 @@ def test_binding_output_checks():
         binding._workspace(torch.zeros(512), 512, cpu)
     assert binding._workspace(None, 0, cpu) is None
     assert binding._workspace(None, 300, cpu).numel() == 300
+
+
+def test_noalloc_validation(lib):
+    """fa_bwd_noalloc validates like fa_bwd_ex and refuses problems beyond its
+    static scratch (2^21 query rows) before any HIP call."""
+    Q = [0x100000000 * (i + 1) for i in range(10)]  # 4 GiB apart: nothing overlaps
+    args = dict(B=2048, H=1, Hkv=1, Nq=1024, Nk=64, d=64, scale=0.125, causal=1, window=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.fa_bwd_noalloc(*Q[:9], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                  a["causal"], a["window"], None)
+    assert call(B=2049) == -10                       # 2^21 + 1024 rows
+    assert call(scale=float("nan")) == -7            # 2^21 rows fit
+    assert call(d=96) == -3
+    assert call(Hkv=3, H=4) == -2
+    assert call(window=-1) == -9
+    assert lib.fa_bwd_noalloc(None, *Q[1:9], 1, 1, 1, 64, 64, 64, 0.125, 1, 0, None) == -1
