@@ -111,9 +111,9 @@ def read_traffic():
 
 HBM_COMMANDS = [
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/hbm_fetch -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --no-workloads --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/hbm_write -o p -- "
-    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --no-workloads --copy-calibration",
+    "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline --no-next --copy-calibration",
     "python3 bench.py --hbm-summary rocprof_out/hbm_fetch rocprof_out/hbm_write",
 ]
 
@@ -163,9 +163,16 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     gib_kib = 2.0 ** 20
     f_scale, w_scale = gib_kib / f_copy, gib_kib / w_copy
     bwd_alg = bwd_algorithmic_bytes(BWD)
+    c2 = dict(B=4, H=16, N=2048, d=64, causal=False)
+    c3 = dict(B=2, H=32, N=8192, d=128, causal=True)
     kernels = [
         ("fwd", FWD_KERNEL, FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG,
          FWD_KERNEL_DESC, FWD["name"], fwd_algorithmic_bytes(FWD)),
+        ("fwd_d64", "fwd_kernel<64, 4, 64, false, false>", 4 * 16 * (2048 // 128) * 256,
+         "fwd_kernel<64,4,64,false,false> (4 waves, 128 query rows per workgroup)", "fwd_b4_h16_n2048_d64",
+         fwd_algorithmic_bytes(c2)),
+        ("fwd_n8192", FWD_KERNEL, 2 * 32 * (-(-8192 // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG, FWD_KERNEL_DESC,
+         "fwd_b2_h32_n8192_d128_causal_peaked", fwd_algorithmic_bytes(c3)),
         ("bwd_dq", BWD_DQ_KERNEL, BWD["B"] * BWD["H"] * (BWD["N"] // 256) * 512,
          "bwd_dq_kernel<128,8,64,true,false> (dQ and the row terms; 8 waves, 256 query rows per workgroup)",
          BWD["name"], bwd_alg["dq"]),
@@ -195,7 +202,9 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     calib = {"copy_1gib_fetch_kib_raw": round(f_copy, 1), "copy_1gib_write_kib_raw": round(w_copy, 1),
              "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
              "copy_launches": {"fetch": ncf, "write": ncw}}
-    fwd = dict(recs["fwd"], kernel_source_hash=kernel_source_hash(), **calib, commands=HBM_COMMANDS)
+    fwd = dict(recs["fwd"], kernel_source_hash=kernel_source_hash(), **calib, commands=HBM_COMMANDS,
+               other_forward_workloads={"fwd_b4_h16_n2048_d64": recs["fwd_d64"],
+                                        "fwd_b2_h32_n8192_d128_causal_peaked": recs["fwd_n8192"]})
     bwd = {"kernel_source_hash": kernel_source_hash(BWD_KERNEL_SOURCES), "dq": recs["bwd_dq"],
            "main": recs["bwd_main"], **calib, "commands": HBM_COMMANDS}
     return {"fwd": fwd, "bwd": bwd}
@@ -299,10 +308,13 @@ def stats_summary(d: str) -> str:
         key = (r["Kernel_Name"], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), r["Workgroup_Size_X"],
                r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")), r["LDS_Block_Size"])
         per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    def short(name):  # library kernels (torch's random fill) carry very long template names
+        return name if len(name) <= 100 else name[:90] + " ..."
+
     out = ["## --stats (all dispatches of the run)", "", "| kernel | calls | avg ms | total ms | % |",
            "|---|---|---|---|---|"]
     for r in stats:
-        out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                    f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
     out += ["", "## per launch shape (from the kernel trace)", "",
             "| kernel | workgroups | threads / WG | VGPRs | LDS bytes | dispatches | avg ms | avg ms after the first "
@@ -310,7 +322,7 @@ def stats_summary(d: str) -> str:
             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for (k, wgs, wgsz, vg, lds), v in per.items():
         rest = v[1:] or v
-        out.append(f"| `{k}` | {wgs} | {wgsz} | {vg} | {lds} | {len(v)} | {sum(v) / len(v):.4f} | "
+        out.append(f"| `{short(k)}` | {wgs} | {wgsz} | {vg} | {lds} | {len(v)} | {sum(v) / len(v):.4f} | "
                    f"{sum(rest) / len(rest):.4f} | {sorted(v)[len(v) // 2]:.4f} | {min(v):.4f} | {max(v):.4f} |")
     out += ["", "The first dispatch of a kernel in the process runs cold (code and caches); bench.py's "
             "roofline times the launches after its warmup, so it compares with the average after the first."]

@@ -26,7 +26,10 @@
 //  * softmax works in base 2 with scale*log2(e) folded into one FMA; the
 //    running maximum is only moved (and O rescaled) when it grows by more
 //    than 2^8, which keeps the result exact (O and the sum share the stale
-//    maximum) and skips most rescale passes;
+//    maximum) and skips most rescale passes.  An unmasked tile skips its
+//    own maximum once every row has a finite one and runs again with it
+//    only when some probability exceeds 2^8 (when the rescale would move
+//    the maximum);
 //  * masks: key j is visible to query i iff i + off - wl <= j <= i + off + wr
 //    (off = N_k - N_q); causal is wr = 0 with wl unbounded, a sliding window
 //    of W keys bounds wl (and, not causal, wr) by W - 1.  Key tiles outside
@@ -199,84 +202,103 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
   auto scores_softmax = [&](auto MASK, int kb, const lds_char* kt_lds, uint32_t (&pk)[NSB][8])
       __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(MASK)::value;
-    // S^T (keys x queries) for each 32-key sub-block: NSB * NKK products in
-    // one stream, the K operand of product j + KA requested from LDS when
-    // product j issues (a ring of KA + 1 operands).  The scheduling barriers
-    // keep the compiler from pulling the reads back to their use, which
-    // would make each product wait out a full LDS latency.  With three
-    // waves per SIMD the other waves cover most of that latency, and the
-    // registers of a deeper ring are not there (KA = 1); with two, KA = 4.
-    constexpr int KA = NW >= 12 ? 1 : 4;
-    f32x16 sacc[NSB];
-    {
-      constexpr int NJ = NSB * NKK;
-      bf16x8 ring[KA + 1];
-      auto read_k = [&](int j) __attribute__((always_inline)) {
-        ring[j % (KA + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff(j % NKK));
-      };
+    // The row maximum only serves as the reference point of the
+    // exponentials.  Once every row of the wave has a finite running
+    // maximum, an unmasked tile skips its own maximum and takes the
+    // probabilities against the running one.  If some row's tile sum then
+    // exceeds 2^8, the tile runs again from its scores with the maximum.
+    // Otherwise every probability is at most 2^8, exactly the case in which
+    // the lazy rescale below would have kept the stale maximum as well: the
+    // probabilities are the ones the path with the maximum computes.
+    bool with_max = MASKED || __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) != 0;
+    for (;;) {
+      // S^T (keys x queries) for each 32-key sub-block: NSB * NKK products in
+      // one stream, the K operand of product j + KA requested from LDS when
+      // product j issues (a ring of KA + 1 operands).  The scheduling barriers
+      // keep the compiler from pulling the reads back to their use, which
+      // would make each product wait out a full LDS latency.  With three
+      // waves per SIMD the other waves cover most of that latency, and the
+      // registers of a deeper ring are not there (KA = 1); with two, KA = 4.
+      constexpr int KA = NW >= 12 ? 1 : 4;
+      f32x16 sacc[NSB];
+      {
+        constexpr int NJ = NSB * NKK;
+        bf16x8 ring[KA + 1];
+        auto read_k = [&](int j) __attribute__((always_inline)) {
+          ring[j % (KA + 1)] = lds_read16(kt_lds + (j / NKK) * 32 * ROWB + koff(j % NKK));
+        };
 #pragma unroll
-      for (int j = 0; j < KA && j < NJ; ++j) read_k(j);
+        for (int j = 0; j < KA && j < NJ; ++j) read_k(j);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+        for (int j = 0; j < NJ; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + KA < NJ) read_k(j + KA);
+          __builtin_amdgcn_sched_barrier(0);
+          const int sb = j / NKK, kk = j % NKK;
+          sacc[sb] = mfma32(ring[j % (KA + 1)], qop[kk], kk == 0 ? f32x16{} : sacc[sb]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (j + KA < NJ) read_k(j + KA);
-        __builtin_amdgcn_sched_barrier(0);
-        const int sb = j / NKK, kk = j % NKK;
-        sacc[sb] = mfma32(ring[j % (KA + 1)], qop[kk], kk == 0 ? f32x16{} : sacc[sb]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
 
-    // mask on tiles crossing a band edge: invisible key -> -inf.  The scale
-    // factor c is never 0 (the host clamps it to a tiny positive number), so
-    // exp2(-inf * c - m) below is exactly 0 with no second mask.
-    if constexpr (MASKED) {
-      // key outside [qrow + lo_off, qrow + hi_off], or key >= Nk (past the keys)
-      const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;
-      const int lo = qrow + lo_off;
+      if (with_max) {
+        // mask on tiles crossing a band edge: invisible key -> -inf.  The scale
+        // factor c is never 0 (the host clamps it to a tiny positive number), so
+        // exp2(-inf * c - m) below is exactly 0 with no second mask.
+        if constexpr (MASKED) {
+          // key outside [qrow + lo_off, qrow + hi_off], or key >= Nk (past the keys)
+          const int hi = BAND ? min(qrow + hi_off, a.Nk - 1) : a.Nk - 1;
+          const int lo = qrow + lo_off;
+#pragma unroll
+          for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
+              const bool out = WIN ? (key > hi || key < lo) : key > hi;
+              sacc[sb][e] = out ? -__builtin_inff() : sacc[sb][e];
+            }
+        }
+        // row max of this tile (raw scores), then in scaled base-2 units
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
+        mx = max_cross_half(mx);
+        const float mblk = (mx == -__builtin_inff()) ? mx : mx * c;
+        const float mnew = fmaxf(m_run, mblk);
+        const bool need = mnew > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float alpha = need ? fast_exp2(m_run - mnew) : 1.0f;
+          if (need) m_run = mnew;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+          l_run *= alpha;
+        }
+      }
+
+      // probabilities, rounded to bf16 pairs for the PV product.  Only a masked
+      // tile can leave a row without a key so far (m = -inf, every p = 0); after
+      // an unmasked tile m is finite.
+      const float negm = (MASKED && m_run == -__builtin_inff()) ? 0.f : -m_run;
+      float lt = 0.f;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * sb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-          const bool out = WIN ? (key > hi || key < lo) : key > hi;
-          sacc[sb][e] = out ? -__builtin_inff() : sacc[sb][e];
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
+          const float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
+          lt += p0 + p1;
+          pk[sb][e >> 1] = pack_bf16x2(p0, p1);
         }
-    }
-
-    // row max of this tile (raw scores), then in scaled base-2 units
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
-    mx = max_cross_half(mx);
-    const float mblk = (mx == -__builtin_inff()) ? mx : mx * c;
-    const float mnew = fmaxf(m_run, mblk);
-    const bool need = mnew > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_run - mnew) : 1.0f;
-      if (need) m_run = mnew;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      l_run *= alpha;
-    }
-
-    // probabilities, rounded to bf16 pairs for the PV product.  Only a masked
-    // tile can leave a row without a key so far (m = -inf, every p = 0); after
-    // an unmasked tile m is finite.
-    const float negm = (MASKED && m_run == -__builtin_inff()) ? 0.f : -m_run;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(fmaf(sacc[sb][e], c, negm));
-        const float p1 = fast_exp2(fmaf(sacc[sb][e + 1], c, negm));
-        l_run += p0 + p1;
-        pk[sb][e >> 1] = pack_bf16x2(p0, p1);
+      if (!with_max && __builtin_amdgcn_ballot_w64(!(lt <= 256.0f)) != 0) {
+        with_max = true;
+        continue;
       }
+      l_run += lt;
+      break;
+    }
   };
   // O^T += V^T P^T over the tile's keys, 16 at a time; the V^T operands of
   // one key step are all requested before its products

@@ -156,16 +156,23 @@ def _probabilities(q, k, scale, causal, window=0):
     return e / np.where(tot > 0, tot, 1.0)
 
 
-def forward_error_bound(q, k, v, scale, causal, window=0):
-    """Per-element bound for O, layout [B, N, H, d] (K, V may have fewer heads)."""
+def forward_error_bound(q, k, v, scale, causal, window=0, workers=1):
+    """Per-element bound for O, layout [B, N, H, d] (K, V may have fewer heads);
+    the heads spread over ``workers`` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
     B, N, H, d = q.shape
     G = H // k.shape[2]
     out = np.empty((B, N, H, v.shape[3]))
-    for b in range(B):
-        for h in range(H):
-            p = _probabilities(q[b, :, h].astype(np.float64), k[b, :, h // G].astype(np.float64), scale, causal,
-                               window)
-            out[b, :, h] = 2 * U_BF16 * (p @ np.abs(v[b, :, h // G].astype(np.float64)))
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        p = _probabilities(q[b, :, h].astype(np.float64), k[b, :, h // G].astype(np.float64), scale, causal,
+                           window)
+        out[b, :, h] = 2 * U_BF16 * (p @ np.abs(v[b, :, h // G].astype(np.float64)))
+
+    with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(one, range(B * H)))
     return out
 
 

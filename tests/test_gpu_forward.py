@@ -142,3 +142,37 @@ def test_workload_fwd_b1_h32_n32768_d128_causal(fa):
     announce("fwd workload B=1 H=32 N=32768 d=128 causal (every element)")
     inp = make_workload("fwd_b1_h32_n32768_d128_causal")
     check_workload_every_element(fa, inp, 1.0 / math.sqrt(128))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_running_max_jumps(fa, causal):
+    """Unmasked tiles take their probabilities against the running maximum
+    and run again with their own maximum when one would exceed 2^12.  Here
+    one key row per head, far into the sequence, is scaled x16 (exact in
+    bf16): every row that sees it meets a score more than 12 (base 2) above
+    its running maximum in an unmasked tile.  The grid (2 x 32 heads of 6144
+    rows) is large enough for the 12-wave causal kernel.  Every element.
+    Outside the workloads, so O is held to the bound derived from the bf16
+    arithmetic (parity.py): a dominant key up to 8 (base 2) above the
+    reference keeps a probability up to 2^8 whose bf16 rounding (relative
+    2^-8) enters O in full, beyond the fixed 1e-2 gate when |V| is large."""
+    from io_aware_tiled_fa_amd.inputs import bf16_bits_from_f32, f32_from_bf16_bits
+    from parity import oracle_forward_by_head
+
+    announce(f"fwd running-max jumps causal={causal}")
+    inp = make_inputs(2, 32, 6144, 128, seed=4711)
+    k = f32_from_bf16_bits(inp.k_bits).copy()
+    k[:, 2500] *= 16.0
+    k[:, 5000] *= 16.0
+    inp.k_bits = bf16_bits_from_f32(k)
+    inp._cache.clear()
+    import os
+
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_fwd(fa, inp, causal, scale)
+    o_ref, lse_ref = oracle_forward_by_head(inp, scale, causal)
+    bound = forward_error_bound(inp.q, inp.k, inp.v, scale, causal,
+                                workers=max(1, min(16, len(os.sched_getaffinity(0)))))
+    compare("O", to_numpy_f32(o), o_ref, TOL_O, bound=bound)
+    compare("LSE", lse.cpu().numpy(), lse_ref, TOL_LSE, ulp_aware=False)
