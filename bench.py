@@ -168,8 +168,9 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     kernels = [
         ("fwd", FWD_KERNEL, FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG,
          FWD_KERNEL_DESC, FWD["name"], fwd_algorithmic_bytes(FWD)),
-        ("fwd_d64", "fwd_kernel<64, 4, 64, false, false>", 4 * 16 * (2048 // 128) * 256,
-         "fwd_kernel<64,4,64,false,false> (4 waves, 128 query rows per workgroup)", "fwd_b4_h16_n2048_d64",
+        ("fwd_d64", "fwd_kernel<64, 4, 64, true, false>", 4 * 16 * (2048 // 128) * 256,
+         "fwd_kernel<64,4,64,true,false> (4 waves, 128 query rows per workgroup, unbounded band)",
+         "fwd_b4_h16_n2048_d64",
          fwd_algorithmic_bytes(c2)),
         ("fwd_n8192", FWD_KERNEL, 2 * 32 * (-(-8192 // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG, FWD_KERNEL_DESC,
          "fwd_b2_h32_n8192_d128_causal_peaked", fwd_algorithmic_bytes(c3)),

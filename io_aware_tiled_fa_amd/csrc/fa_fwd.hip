@@ -52,7 +52,7 @@ namespace fa {
 // BAND: the visible keys have an upper edge (causal, or a window); WIN: they
 // also have a lower edge (a window).  Without BAND every key is visible.
 template <int D, int NW, int BC, bool BAND, bool WIN>
-__global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (D == 64 ? 4 : (NW / 4 > 2 ? NW / 4 : 2))) void fwd_kernel(FwdArgs a) {
   static_assert(BAND || !WIN, "a window always bounds the keys above");
   constexpr int BR = NW * 32;
   constexpr int ROWB = D * 2;            // bytes of one tile row in LDS
@@ -216,10 +216,10 @@ __global__ __launch_bounds__(NW * 64, (NW / 4 > 2 ? NW / 4 : 2)) void fwd_kernel
       // one stream, the K operand of product j + KA requested from LDS when
       // product j issues (a ring of KA + 1 operands).  The scheduling barriers
       // keep the compiler from pulling the reads back to their use, which
-      // would make each product wait out a full LDS latency.  With three
-      // waves per SIMD the other waves cover most of that latency, and the
-      // registers of a deeper ring are not there (KA = 1); with two, KA = 4.
-      constexpr int KA = NW >= 12 ? 1 : 4;
+      // would make each product wait out a full LDS latency.  With three or
+      // four waves per SIMD the other waves cover most of that latency, and
+      // the registers of a deeper ring are not there (KA = 1); with two, KA = 4.
+      constexpr int KA = (NW >= 12 || D == 64) ? 1 : 4;
       f32x16 sacc[NSB];
       {
         constexpr int NJ = NSB * NKK;
@@ -405,7 +405,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 // shrinks the workgroup count of a short sequence by a third, so it is used
 // only where at least 1024 workgroups remain (four per CU); otherwise, and
 // for full attention (whose kernel needs more registers), 8 waves of 256
-// rows run two per SIMD.  d = 64: 4 waves (128 rows).
+// rows run two per SIMD.  d = 64: 4 waves (128 rows) at four waves per SIMD
+// (at most 128 registers), four workgroups per CU; full attention runs the
+// banded kernel with an unbounded band, which masks only the ragged last
+// tile and fits those registers (the unbanded one needs 142).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
   if (d == 128) {
     if (!band) return launch_fwd_t<128, 8, 64, false, false>(a, stream);
@@ -414,7 +417,7 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t 
     return big ? launch_fwd_t<128, 12, 64, true, false>(a, stream) : launch_fwd_t<128, 8, 64, true, false>(a, stream);
   }
   if (win) return launch_fwd_t<64, 4, 64, true, true>(a, stream);
-  return band ? launch_fwd_t<64, 4, 64, true, false>(a, stream) : launch_fwd_t<64, 4, 64, false, false>(a, stream);
+  return launch_fwd_t<64, 4, 64, true, false>(a, stream);
 }
 
 }  // namespace fa
