@@ -4,7 +4,6 @@ LSE; the oracle recomputes everything from Q, K, V and dO in fp64."""
 
 import math
 
-import numpy as np
 import pytest
 
 import oracle

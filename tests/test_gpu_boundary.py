@@ -11,7 +11,6 @@ scale defaulting to 1/sqrt(head_dim) and a causal flag (holysheep.ai review,
 
 import math
 
-import numpy as np
 import pytest
 
 import oracle

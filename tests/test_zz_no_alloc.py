@@ -6,7 +6,6 @@ problems beyond its scratch before launching anything."""
 
 import math
 
-import numpy as np
 import pytest
 
 from io_aware_tiled_fa_amd.inputs import make_inputs
