@@ -168,8 +168,8 @@ def hbm_summary(fetch_dir: str, write_dir: str) -> dict:
     kernels = [
         ("fwd", FWD_KERNEL, FWD["B"] * FWD["H"] * (-(-FWD["N"] // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG,
          FWD_KERNEL_DESC, FWD["name"], fwd_algorithmic_bytes(FWD)),
-        ("fwd_d64", "fwd_kernel<64, 4, 64, true, false>", 4 * 16 * (2048 // 128) * 256,
-         "fwd_kernel<64,4,64,true,false> (4 waves, 128 query rows per workgroup, unbounded band)",
+        ("fwd_d64", "fwd_kernel<64, 8, 64, true, false>", 4 * 16 * (2048 // 256) * 512,
+         "fwd_kernel<64,8,64,true,false> (8 waves, 256 query rows per workgroup, unbounded band)",
          "fwd_b4_h16_n2048_d64",
          fwd_algorithmic_bytes(c2)),
         ("fwd_n8192", FWD_KERNEL, 2 * 32 * (-(-8192 // FWD_ROWS_PER_WG)) * FWD_THREADS_PER_WG, FWD_KERNEL_DESC,
@@ -425,8 +425,8 @@ def main(argv=None):
                     "launch of 2752 workgroups of 768 threads; the fwd_kernel<128, 8, ...> launch of 1024 "
                     "workgroups is the setup forward of the backward batch) and fa_bwd on B=4 H=16 N=4096 "
                     "d=128 causal (bwd_dq_kernel = dQ and the row terms, then bwd_main_kernel = dK/dV); "
-                    "then the other forward workloads (B=4 H=16 N=2048 d=64: fwd_kernel<64, 4, ...> of "
-                    "1024 workgroups; B=2 H=32 N=8192 d=128 causal peaked: fwd_kernel<128, 12, ...> of "
+                    "then the other forward workloads (B=4 H=16 N=2048 d=64: fwd_kernel<64, 8, ...> of "
+                    "512 workgroups; B=2 H=32 N=8192 d=128 causal peaked: fwd_kernel<128, 12, ...> of "
                     "1408 workgroups) and the extension configurations of the bench line's `next` "
                     "(cross attention, grouped K/V heads forward and backward, a 4096-key window, split-KV "
                     "decoding: decode_kernel and decode_combine_kernel, and the general forward on the "

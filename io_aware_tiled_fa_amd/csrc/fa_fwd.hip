@@ -405,10 +405,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 // shrinks the workgroup count of a short sequence by a third, so it is used
 // only where at least 1024 workgroups remain (four per CU); otherwise, and
 // for full attention (whose kernel needs more registers), 8 waves of 256
-// rows run two per SIMD.  d = 64: 4 waves (128 rows) at four waves per SIMD
-// (at most 128 registers), four workgroups per CU; full attention runs the
-// banded kernel with an unbounded band, which masks only the ragged last
-// tile and fits those registers (the unbanded one needs 142).
+// rows run two per SIMD.  d = 64: four waves per SIMD (at most 128
+// registers); full attention runs the banded kernel with an unbounded band,
+// which masks only the ragged last tile and fits those registers (the
+// unbanded one needs 142).  Workgroups of 4 waves (128 rows, four per CU),
+// or of 8 waves (256 rows, two per CU, each K/V tile copied once for twice
+// the rows) for full attention when those fill the chip at least once (512
+// workgroups): 8 waves measured 4-6% faster there, and slower on causal
+// grids (coarser tiles on the diagonal) and on small grids.
 hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t stream) {
   if (d == 128) {
     if (!band) return launch_fwd_t<128, 8, 64, false, false>(a, stream);
@@ -417,6 +421,7 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool band, bool win, hipStream_t 
     return big ? launch_fwd_t<128, 12, 64, true, false>(a, stream) : launch_fwd_t<128, 8, 64, true, false>(a, stream);
   }
   if (win) return launch_fwd_t<64, 4, 64, true, true>(a, stream);
+  if (!band && (long)a.B * a.H * ((a.Nq + 255) / 256) >= 512) return launch_fwd_t<64, 8, 64, true, false>(a, stream);
   return launch_fwd_t<64, 4, 64, true, false>(a, stream);
 }
 

@@ -128,3 +128,23 @@ def test_forward_large_grid_ragged(fa, B, H, Nq, Nk):
     o_ref, lse_ref = oracle_forward_by_head(inp, 1.0 / math.sqrt(128), True)
     compare("O", to_numpy_f32(o), o_ref, TOL_O, TOL_O_MEAN)
     compare("LSE", lse.cpu().numpy(), lse_ref, TOL_LSE, ulp_aware=False)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,H,Nq,Nk", [(4, 16, 2000, 2000), (4, 16, 1900, 2100)])
+def test_forward_d64_large_grid_ragged(fa, B, H, Nq, Nk):
+    """Full attention at d = 64 on grids of at least 512 workgroups of 256
+    rows runs the 8-wave d = 64 kernel; these end ragged in its 256-row query
+    tiles and 64-key tiles.  Every element against the oracle."""
+    import torch
+
+    from parity import TOL_LSE, TOL_O, TOL_O_MEAN, compare, oracle_forward_by_head, to_numpy_f32
+
+    announce(f"fwd d=64 large grid B={B} H={H} Nq={Nq} Nk={Nk} full attention (every element)")
+    inp = make_inputs(B, H, Nq, 64, N_k=Nk, seed=6400 + Nq)
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o, lse = fa.forward(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_forward_by_head(inp, 1.0 / math.sqrt(64), False)
+    compare("O", to_numpy_f32(o), o_ref, TOL_O, TOL_O_MEAN)
+    compare("LSE", lse.cpu().numpy(), lse_ref, TOL_LSE, ulp_aware=False)
