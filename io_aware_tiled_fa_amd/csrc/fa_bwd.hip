@@ -386,8 +386,11 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // ---- consumers: waves 4 and 5 add dV^T += dO^T P for keys 0-63 and
   // 64-127 of the block, waves 6 and 7 dK^T += Q^T dS for the same halves.
   // Each transpose read of dO or Q then feeds two products (one per 32-key
-  // group of the half).  Accumulators: [group of the half][db], lane holds
-  // [key 8(e/4)+4h2+e%4][d = 32 db + l32].
+  // group of the half).  The products are formed transposed (dO / Q
+  // columns as the A operand, P^T / dS^T as B), so the accumulators
+  // [group of the half][db] hold dV^T / dK^T: lane [d = 32 db + 8(e/4) + 4h2
+  // + e%4][key 32 g + l32], four consecutive d per lane and key, which the
+  // epilogue stores as one 8-byte piece.
   const int kh = w & 1;             // key half of this consumer
   const int kw2 = kb + 64 * kh;     // its first key
   f32x16 acc[2][NDB];
@@ -435,8 +438,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
       if (i + CD < NP) read_op(i + CD);
       __builtin_amdgcn_sched_barrier(0);
       const int tq = i / NDB, db = i % NDB, s = i % (CD + 1);
-      acc[0][db] = mfma32(pa[0][tq & 1], xo[s], acc[0][db]);
-      acc[1][db] = mfma32(pa[1][tq & 1], xo[s], acc[1][db]);
+      acc[0][db] = mfma32(xo[s], pa[0][tq & 1], acc[0][db]);
+      acc[1][db] = mfma32(xo[s], pa[1][tq & 1], acc[1][db]);
     }
   };
   const bool half_active = kw2 < a.Nk;
@@ -465,20 +468,25 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   else
     walk(std::false_type{});
 
-  // ---- consumer epilogue: dV = dV_acc, or dK = scale dK_acc
+  // ---- consumer epilogue: dV = dV_acc, or dK = scale dK_acc, four
+  // consecutive d of one key per 8-byte store
   if (!half_active) return;
   const float f = dv_role ? 1.0f : a.scale;
   __bf16* out = dv_role ? a.dv : a.dk;
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < 2; ++g) {
+    const int kr = kw2 + 32 * g + l32;
+    if (kr >= a.Nk) continue;
+    __bf16* orow = out + kv_off + (size_t)kr * rk;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kr = kw2 + 32 * g + 8 * (e >> 2) + 4 * h2 + (e & 3);
-        if (kr >= a.Nk) continue;
-        out[kv_off + (size_t)kr * rk + 32 * db + l32] = (__bf16)(acc[g][db][e] * f);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h2;
+        *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(acc[g][db][4 * g4] * f, acc[g][db][4 * g4 + 1] * f),
+                                     pack_bf16x2(acc[g][db][4 * g4 + 2] * f, acc[g][db][4 * g4 + 3] * f)};
       }
+  }
 }
 
 // ---------------------------------------------------------------------------
