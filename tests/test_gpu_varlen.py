@@ -91,6 +91,18 @@ def test_backward_cross(fa, B, H, Nq, Nk, d, causal):
     check_backward(fa, inp, causal, 1.0 / math.sqrt(d))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(2, 8, 1100, 1100, 64, True), (1, 16, 900, 1300, 64, False),
+                                                 (2, 8, 1500, 1500, 128, True)])
+def test_backward_grid_ragged(fa, B, H, Nq, Nk, d, causal):
+    """Backward on grids whose (batch, head) count is a multiple of 8, so
+    both kernels take the per-XCD head order, over several workgroup rounds
+    and ragged in every tile size.  Every element under the error model."""
+    announce(f"bwd grid B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    inp = make_inputs(B, H, Nq, d, N_k=Nk, seed=7000 + Nq + Nk + d, with_do=True)
+    check_backward(fa, inp, causal, 1.0 / math.sqrt(d))
+
+
 def test_cross_equals_suffix_of_self(fa):
     """Causal cross attention of the last N_q queries over N_k keys equals the
     last N_q rows of causal self-attention over all N_k positions, bit for
