@@ -1,7 +1,7 @@
 """Render the per-check statistics of a GPU test run as a markdown table.
 
-    FA_PARITY_STATS=gpurun_out/parity_stats.jsonl python -m pytest tests -m gpu -s ...
-    python tests/parity_report.py gpurun_out/parity_stats.jsonl profiles/parity_stats.md
+    FA_PARITY_STATS=/tmp/parity_stats.jsonl python -m pytest tests -m gpu -s ...
+    python tests/parity_report.py /tmp/parity_stats.jsonl profiles/parity_stats.md
 
 Each line of the input is one comparison of a GPU result with the fp64
 oracle (parity.compare / parity.compare_model): the raw max-abs and
@@ -30,8 +30,8 @@ reference), LSE to 1e-3, and every other gradient to the error model of
 Commands (repo root, MI355X):
 
 ```
-FA_PARITY_STATS=gpurun_out/parity_stats.jsonl python -u -m pytest tests -m gpu -x -v -s --timeout 900 --timeout-method thread
-python tests/parity_report.py gpurun_out/parity_stats.jsonl profiles/parity_stats.md
+FA_PARITY_STATS=/tmp/parity_stats.jsonl python -u -m pytest tests -m gpu -x -v -s --timeout 900 --timeout-method thread
+python tests/parity_report.py /tmp/parity_stats.jsonl profiles/parity_stats.md
 ```
 
 """
