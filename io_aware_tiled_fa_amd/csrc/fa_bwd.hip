@@ -468,25 +468,48 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   else
     walk(std::false_type{});
 
-  // ---- consumer epilogue: dV = dV_acc, or dK = scale dK_acc, four
-  // consecutive d of one key per 8-byte store
+  // ---- consumer epilogue: dV = dV_acc, or dK = scale dK_acc, in bf16.
+  // A lane holds four consecutive d of one key per 8-byte piece, so storing
+  // the accumulators directly would spread every store instruction over 32
+  // key rows in 16-byte pieces.  They go through LDS instead (each wave's
+  // 64 keys into the Q and dO buffers of its own index, rows of 2 D bytes
+  // with the 16-byte pieces of row r at piece ^ (r mod D / 8)) and are
+  // read back a row per D / 8 lanes, so each store instruction writes whole
+  // rows.  The barrier waits for the other consumers' last reads of those
+  // buffers (the producers have ended and no longer count).
+  barrier_lds();
   if (!half_active) return;
+  constexpr int NCH = D / 8;  // 16-byte pieces of a row
   const float f = dv_role ? 1.0f : a.scale;
   __bf16* out = dv_role ? a.dv : a.dk;
+  const int ci = w & 3;
+  lds_char* stage[2] = {(lds_char*)(ci == 0 ? q_lds0 : ci == 1 ? q_lds1 : ci == 2 ? q_lds2 : q_lds3),
+                        (lds_char*)(ci == 0 ? g_lds0 : ci == 1 ? g_lds1 : ci == 2 ? g_lds2 : g_lds3)};
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int kr = kw2 + 32 * g + l32;
-    if (kr >= a.Nk) continue;
-    __bf16* orow = out + kv_off + (size_t)kr * rk;
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * h2;
-        *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(acc[g][db][4 * g4] * f, acc[g][db][4 * g4 + 1] * f),
-                                     pack_bf16x2(acc[g][db][4 * g4 + 2] * f, acc[g][db][4 * g4 + 3] * f)};
+        // d = 32 db + 8 g4 + 4 h2 .. + 3 of key row l32: piece 4 db + g4, half h2
+        const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
+        *(lds_u32x2*)(stage[g] + off) = u32x2{pack_bf16x2(acc[g][db][4 * g4] * f, acc[g][db][4 * g4 + 1] * f),
+                                              pack_bf16x2(acc[g][db][4 * g4 + 2] * f, acc[g][db][4 * g4 + 3] * f)};
       }
-  }
+  // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
+  constexpr int RPI = 64 / NCH;  // rows per store instruction
+  const int pc = l % NCH;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + l / NCH;
+      const u32x4 v = *(const lds_u32x4*)(stage[g] + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+      const int kr = kw2 + 32 * g + r;
+      if (kr < a.Nk) *(u32x4*)(out + kv_off + (size_t)kr * rk + 8 * pc) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -777,19 +800,38 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       tile_step(std::true_type{}, nloop, K0, V0, K1, V1);
   }
 
-  if (!row_valid) return;
-  // ---- dQ = scale dQ^T; lane holds [d = 32 db + 8(e/4)+4h2+e%4][query l32]
+  // ---- dQ = scale dQ^T; lane holds [d = 32 db + 8(e/4)+4h2+e%4][query l32].
+  // As in the dK / dV kernel's epilogue, the rows go through LDS (each
+  // wave's 32 rows into its own quarter of the K / V buffers, 16-byte
+  // pieces of row r at piece ^ (r mod D / 8)) so that each store
+  // instruction writes whole rows.  The barrier waits for the last tile's
+  // reads.
+  barrier_lds();
+  if (!wave_active) return;
+  constexpr int NCH = D / 8;  // 16-byte pieces of a row
+  static_assert(4 * TILEB >= NW * 32 * ROWB, "the K / V buffers must hold every wave's rows");
   const float scale = a.scale;
-  __bf16* dqrow = a.dq + q_off + (size_t)qrow * rs;
+  lds_char* stage = (lds_char*)(w < NW / 4 ? k_lds0 : w < NW / 2 ? k_lds1 : w < 3 * NW / 4 ? v_lds0 : v_lds1) +
+                    (w % (NW / 4)) * 32 * ROWB;
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * db + 8 * g4 + 4 * h2;
-      u32x2 val = {pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
-                   pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
-      *(u32x2*)(dqrow + d0) = val;
+      const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
+      *(lds_u32x2*)(stage + off) = u32x2{pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
+                                         pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
     }
+  // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
+  constexpr int RPI = 64 / NCH;
+  const int pc = l % NCH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + l / NCH;
+    const u32x4 v = *(const lds_u32x4*)(stage + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+    if (qw + r < a.Nq) *(u32x4*)(a.dq + q_off + (size_t)(qw + r) * rs + 8 * pc) = v;
+  }
 }
 
 template <int D, bool BAND, bool WIN>
