@@ -370,24 +370,64 @@ __global__ __launch_bounds__(NW * 64, (D == 64 ? 4 : (NW / 4 > 2 ? NW / 4 : 2)))
     tile_step(std::true_type{}, nloop, odd ? K1 : K0, odd ? V1 : V0, odd ? K0 : K1, odd ? V0 : V1);
   }
 
-  if (!wave_active) return;
   // ---- epilogue: O = O_acc / l in bf16, LSE = (m + log2 l) ln 2; a row
-  // that saw no key gets O = 0 and LSE = -inf
-  const float lt = sum_cross_half(l_run);
-  const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
-  if (!row_valid) return;
-  __bf16* orow = a.o + q_off + (size_t)qrow * rs;
+  // that saw no key gets O = 0 and LSE = -inf.  A lane holds four
+  // consecutive d of its row per 8-byte piece, so storing O directly
+  // spreads every store instruction over 32 rows in 16-byte pieces.  Where
+  // every wave's 32 rows fit in the K / V buffers (8 waves or fewer) they go
+  // through LDS instead (each wave its own slice, 16-byte pieces of row r at
+  // piece ^ (r mod D / 8)) and are read back a row per D / 8 lanes, so each
+  // store instruction writes whole rows; the barrier waits for the last
+  // tile's reads.  The 12-wave kernel keeps the direct stores: staging in
+  // two passes made the compiler spill inside the key loop.
+  constexpr bool STAGED = NW * 32 <= 4 * BC;
+  if constexpr (STAGED) {
+    __syncthreads();
+    if (!wave_active) return;
+    const float lt = sum_cross_half(l_run);
+    const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
+    if (row_valid && h2 == 0)
+      a.lse[((size_t)b * a.H + h) * a.Nq + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -__builtin_inff();
+    constexpr int WPB = BC / 32;  // waves per buffer
+    lds_char* stage = (lds_char*)(w < WPB ? k_lds0 : w < 2 * WPB ? k_lds1 : w < 3 * WPB ? v_lds0 : v_lds1) +
+                      (w % WPB) * 32 * ROWB;
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * db + 8 * g4 + 4 * h2;
-      u32x2 val = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                   pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-      *(u32x2*)(orow + d0) = val;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
+        *(lds_u32x2*)(stage + off) = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+      }
+    // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
+    constexpr int RPI = 64 / NCH;
+    const int pc = l % NCH;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + l / NCH;
+      const u32x4 v = *(const lds_u32x4*)(stage + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+      if (qw + r < a.Nq) *(u32x4*)(a.o + q_off + (size_t)(qw + r) * rs + 8 * pc) = v;
     }
-  if (h2 == 0)
-    a.lse[((size_t)b * a.H + h) * a.Nq + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -__builtin_inff();
+  } else {
+    if (!wave_active) return;
+    const float lt = sum_cross_half(l_run);
+    const float inv = lt > 0.f ? fast_rcp(lt) : 0.f;
+    if (!row_valid) return;
+    __bf16* orow = a.o + q_off + (size_t)qrow * rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h2;
+        u32x2 val = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                     pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+        *(u32x2*)(orow + d0) = val;
+      }
+    if (h2 == 0)
+      a.lse[((size_t)b * a.H + h) * a.Nq + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -__builtin_inff();
+  }
 }
 
 template <int D, int NW, int BC, bool BAND, bool WIN>
