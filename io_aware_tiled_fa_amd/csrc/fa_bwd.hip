@@ -266,10 +266,10 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // arrivals, so every wave passes one per step.
   if (0 < nv) issue_next(IC<0>{});
   if (1 < nv) issue_next(IC<1>{});
-  step_barrier();
 
   if (producer) {
-    // the group's keys and values as B operands (lane = key l32, d = 16 kk + 8 h2 ..)
+    // the group's keys and values as B operands (lane = key l32, d = 16 kk + 8 h2 ..),
+    // loaded while the consumers' first copies are in flight
     bf16x8 kreg[NKK], vreg[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) kreg[kk] = vreg[kk] = bf16x8{};
@@ -282,6 +282,7 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
         vreg[kk] = *(const bf16x8*)(vr + 16 * kk);
       }
     }
+    step_barrier();
     typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
     // S (lane = key l32, e -> query 8(e/4)+4h2+e%4) and dP - D, the latter
     // accumulated onto -D, of the block in buffer qb4 / row terms rb3.
@@ -382,6 +383,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
     }
     return;
   }
+
+  step_barrier();  // (the consumers' first; the producers passed theirs above)
 
   // ---- consumers: waves 4 and 5 add dV^T += dO^T P for keys 0-63 and
   // 64-127 of the block, waves 6 and 7 dK^T += Q^T dS for the same halves.
@@ -575,44 +578,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbase = a.k + kv_off;
   const __bf16* vbase = a.v + kv_off;
 
-  // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..),
-  // and the row terms: D = dO . O over the lane's half of the row, then
-  // both halves; -D and -L log2(e) also go to the workspace for the dK / dV
-  // kernel, which runs after this one
-  bf16x8 qop[NKK], gop[NKK];
-  float nl = 0.f, ndr = 0.f;  // -L log2(e) and -D of this lane's row
-  float dpart = 0.f;
-  if (row_valid) {
-    const __bf16* qr = a.q + q_off + (size_t)qrow * rs + 8 * h2;
-    const __bf16* gr = a.dO + q_off + (size_t)qrow * rs + 8 * h2;
-    const __bf16* orow = a.o + q_off + (size_t)qrow * rs + 8 * h2;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      qop[kk] = *(const bf16x8*)(qr + 16 * kk);
-      gop[kk] = *(const bf16x8*)(gr + 16 * kk);
-      const u32x4 ov = *(const u32x4*)(orow + 16 * kk);
-      const u32x4 gv = __builtin_bit_cast(u32x4, gop[kk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dpart = fmaf(__builtin_bit_cast(float, ov[i] << 16), __builtin_bit_cast(float, gv[i] << 16), dpart);
-        dpart = fmaf(__builtin_bit_cast(float, ov[i] & 0xFFFF0000u), __builtin_bit_cast(float, gv[i] & 0xFFFF0000u), dpart);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qop[kk] = gop[kk] = bf16x8{};
-  }
-  const float dsum = sum_cross_half(dpart);
-  if (row_valid) {
-    const size_t r = ((size_t)b * a.H + h) * a.Nq + qrow;
-    ndr = -dsum;
-    nl = -a.lse[r] * kLog2e;
-    if (h2 == 0) {
-      a.drow[r] = ndr;
-      a.drow[(size_t)a.B * a.H * a.Nq + r] = nl;
-    }
-  }
-
   // ---- per-lane LDS offsets (K and V tiles in the row-group layout)
   // K / V rows as A operands: row 32 sb + l32, piece 2 kk + h2, at
   // krb[kk & 1] + 256 (kk / 2) + sb 32 ROWB
@@ -656,6 +621,47 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     ntiles = last_key < 0 ? 0 : min(ntiles_all, last_key / BC + 1);
   }
   if (WIN) kt0 = max(0, q0 + lo_off) / BC;                 // first key any row here sees
+  // the first tile's copies go out before the rows below are loaded, so the
+  // two latencies overlap
+  if (kt0 < ntiles) issue_tile(kt0, (lds_char*)k_lds0, (lds_char*)v_lds0);
+
+  // ---- Q and dO rows as B operands (lane: query l32, d = 16 kk + 8 h2 ..),
+  // and the row terms: D = dO . O over the lane's half of the row, then
+  // both halves; -D and -L log2(e) also go to the workspace for the dK / dV
+  // kernel, which runs after this one
+  bf16x8 qop[NKK], gop[NKK];
+  float nl = 0.f, ndr = 0.f;  // -L log2(e) and -D of this lane's row
+  float dpart = 0.f;
+  if (row_valid) {
+    const __bf16* qr = a.q + q_off + (size_t)qrow * rs + 8 * h2;
+    const __bf16* gr = a.dO + q_off + (size_t)qrow * rs + 8 * h2;
+    const __bf16* orow = a.o + q_off + (size_t)qrow * rs + 8 * h2;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qop[kk] = *(const bf16x8*)(qr + 16 * kk);
+      gop[kk] = *(const bf16x8*)(gr + 16 * kk);
+      const u32x4 ov = *(const u32x4*)(orow + 16 * kk);
+      const u32x4 gv = __builtin_bit_cast(u32x4, gop[kk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dpart = fmaf(__builtin_bit_cast(float, ov[i] << 16), __builtin_bit_cast(float, gv[i] << 16), dpart);
+        dpart = fmaf(__builtin_bit_cast(float, ov[i] & 0xFFFF0000u), __builtin_bit_cast(float, gv[i] & 0xFFFF0000u), dpart);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qop[kk] = gop[kk] = bf16x8{};
+  }
+  const float dsum = sum_cross_half(dpart);
+  if (row_valid) {
+    const size_t r = ((size_t)b * a.H + h) * a.Nq + qrow;
+    ndr = -dsum;
+    nl = -a.lse[r] * kLog2e;
+    if (h2 == 0) {
+      a.drow[r] = ndr;
+      a.drow[(size_t)a.B * a.H * a.Nq + r] = nl;
+    }
+  }
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -788,7 +794,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr auto LOOP_MASK = std::integral_constant<bool, BAND>{};
   // (unbanded: kt0 = 0 and the ragged last tile is peeled)
   const int nloop = (!BAND && a.Nk % BC != 0) ? ntiles - 1 : ntiles;
-  if (kt0 < ntiles) issue_tile(kt0, K0, V0);
   for (int kt = kt0; kt < nloop; kt += 2) {
     tile_step(LOOP_MASK, kt, K0, V0, K1, V1);
     if (kt + 1 < nloop) tile_step(LOOP_MASK, kt + 1, K1, V1, K0, V0);
