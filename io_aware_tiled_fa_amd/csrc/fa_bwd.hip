@@ -475,11 +475,11 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
   // A lane holds four consecutive d of one key per 8-byte piece, so storing
   // the accumulators directly would spread every store instruction over 32
   // key rows in 16-byte pieces.  They go through LDS instead (each wave's
-  // 64 keys into the Q and dO buffers of its own index, rows of 2 D bytes
-  // with the 16-byte pieces of row r at piece ^ (r mod D / 8)) and are
-  // read back a row per D / 8 lanes, so each store instruction writes whole
-  // rows.  The barrier waits for the other consumers' last reads of those
-  // buffers (the producers have ended and no longer count).
+  // 64 keys into the Q and dO buffers of its own index, in the staging
+  // layout of fa_layout.h) and are read back a row per D / 8 lanes, so each
+  // store instruction writes whole rows.  The barrier waits for the other
+  // consumers' last reads of those buffers (the producers have ended and no
+  // longer count).
   barrier_lds();
   if (!half_active) return;
   constexpr int NCH = D / 8;  // 16-byte pieces of a row
@@ -497,9 +497,9 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         // d = 32 db + 8 g4 + 4 h2 .. + 3 of key row l32: piece 4 db + g4, half h2
-        const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
-        *(lds_u32x2*)(stage[g] + off) = u32x2{pack_bf16x2(acc[g][db][4 * g4] * f, acc[g][db][4 * g4 + 1] * f),
-                                              pack_bf16x2(acc[g][db][4 * g4 + 2] * f, acc[g][db][4 * g4 + 3] * f)};
+        *(lds_u32x2*)(stage[g] + stage_off<D>(l32, 4 * db + g4, h2)) =
+            u32x2{pack_bf16x2(acc[g][db][4 * g4] * f, acc[g][db][4 * g4 + 1] * f),
+                  pack_bf16x2(acc[g][db][4 * g4 + 2] * f, acc[g][db][4 * g4 + 3] * f)};
       }
   // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
   constexpr int RPI = 64 / NCH;  // rows per store instruction
@@ -509,7 +509,8 @@ __global__ __launch_bounds__(512) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = RPI * i + l / NCH;
-      const u32x4 v = *(const lds_u32x4*)(stage[g] + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+      u32x4 v = *(const lds_u32x4*)(stage[g] + (stage_off<D>(r, pc, 0) & ~15));
+      if (stage_swap<D>(r)) v = u32x4{v[2], v[3], v[0], v[1]};
       const int kr = kw2 + 32 * g + r;
       if (kr < a.Nk) *(u32x4*)(out + kv_off + (size_t)kr * rk + 8 * pc) = v;
     }
@@ -807,10 +808,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // ---- dQ = scale dQ^T; lane holds [d = 32 db + 8(e/4)+4h2+e%4][query l32].
   // As in the dK / dV kernel's epilogue, the rows go through LDS (each
-  // wave's 32 rows into its own quarter of the K / V buffers, 16-byte
-  // pieces of row r at piece ^ (r mod D / 8)) so that each store
-  // instruction writes whole rows.  The barrier waits for the last tile's
-  // reads.
+  // wave's 32 rows into its own quarter of the K / V buffers, in the staging
+  // layout of fa_layout.h) so that each store instruction writes whole
+  // rows.  The barrier waits for the last tile's reads.
   barrier_lds();
   if (!wave_active) return;
   constexpr int NCH = D / 8;  // 16-byte pieces of a row
@@ -824,9 +824,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
-      *(lds_u32x2*)(stage + off) = u32x2{pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
-                                         pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
+      *(lds_u32x2*)(stage + stage_off<D>(l32, 4 * db + g4, h2)) =
+          u32x2{pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
+                pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
     }
   // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
   constexpr int RPI = 64 / NCH;
@@ -834,7 +834,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + l / NCH;
-    const u32x4 v = *(const lds_u32x4*)(stage + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+    u32x4 v = *(const lds_u32x4*)(stage + (stage_off<D>(r, pc, 0) & ~15));
+    if (stage_swap<D>(r)) v = u32x4{v[2], v[3], v[0], v[1]};
     if (qw + r < a.Nq) *(u32x4*)(a.dq + q_off + (size_t)(qw + r) * rs + 8 * pc) = v;
   }
 }

@@ -375,10 +375,10 @@ __global__ __launch_bounds__(NW * 64, (D == 64 ? 4 : (NW / 4 > 2 ? NW / 4 : 2)))
   // consecutive d of its row per 8-byte piece, so storing O directly
   // spreads every store instruction over 32 rows in 16-byte pieces.  Where
   // every wave's 32 rows fit in the K / V buffers (8 waves or fewer) they go
-  // through LDS instead (each wave its own slice, 16-byte pieces of row r at
-  // piece ^ (r mod D / 8)) and are read back a row per D / 8 lanes, so each
-  // store instruction writes whole rows; the barrier waits for the last
-  // tile's reads.  The 12-wave kernel keeps the direct stores: staging in
+  // through LDS instead (each wave its own slice, in the staging layout of
+  // fa_layout.h) and are read back a row per D / 8 lanes, so each store
+  // instruction writes whole rows; the barrier waits for the last tile's
+  // reads.  The 12-wave kernel keeps the direct stores: staging in
   // two passes made the compiler spill inside the key loop.
   constexpr bool STAGED = NW * 32 <= 4 * BC;
   if constexpr (STAGED) {
@@ -397,9 +397,9 @@ __global__ __launch_bounds__(NW * 64, (D == 64 ? 4 : (NW / 4 > 2 ? NW / 4 : 2)))
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int off = l32 * ROWB + (((4 * db + g4) ^ (l32 & (NCH - 1))) << 4) + 8 * h2;
-        *(lds_u32x2*)(stage + off) = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+        *(lds_u32x2*)(stage + stage_off<D>(l32, 4 * db + g4, h2)) =
+            u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                  pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
       }
     // read back: lane l takes piece l % NCH of row 64 / NCH i + l / NCH
     constexpr int RPI = 64 / NCH;
@@ -407,7 +407,8 @@ __global__ __launch_bounds__(NW * 64, (D == 64 ? 4 : (NW / 4 > 2 ? NW / 4 : 2)))
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = RPI * i + l / NCH;
-      const u32x4 v = *(const lds_u32x4*)(stage + r * ROWB + ((pc ^ (r & (NCH - 1))) << 4));
+      u32x4 v = *(const lds_u32x4*)(stage + (stage_off<D>(r, pc, 0) & ~15));
+      if (stage_swap<D>(r)) v = u32x4{v[2], v[3], v[0], v[1]};
       if (qw + r < a.Nq) *(u32x4*)(a.o + q_off + (size_t)(qw + r) * rs + 8 * pc) = v;
     }
   } else {

@@ -79,4 +79,26 @@ __device__ __forceinline__ int pt_off(int row, int q) {
   return row * 64 + (((q >> 2) ^ s) << 3) + 2 * (q & 3);
 }
 
+// Staging of 32 output rows (2 D bytes each) in the epilogues: lane l of a
+// wave holds four consecutive d = 32 db + 8 g4 + 4 (l / 32) .. of row
+// l % 32 and writes them as 8-byte half l / 32 of the row's 16-byte piece
+// 4 db + g4; D / 8 lanes then read each row back a piece apiece.  Piece p
+// of row r sits at slot stage_slot(r, p) of the row, its two halves swapped
+// when stage_swap(r) is set (the reader swaps them back): the 8-byte writes
+// of 16 (32) lanes then land in distinct banks of 32 (64), and so do the
+// 16-byte reads of 8 (16) lanes.
+template <int D>
+__device__ __forceinline__ int stage_slot(int row, int piece) {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  return D == 128 ? piece ^ (row & 15) : piece ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int stage_swap(int row) {
+  return D == 128 ? ((row >> 3) ^ (row >> 4)) & 1 : (row ^ (row >> 4)) & 1;
+}
+template <int D>
+__device__ __forceinline__ int stage_off(int row, int piece, int half) {
+  return row * 2 * D + (stage_slot<D>(row, piece) << 4) + 8 * (half ^ stage_swap<D>(row));
+}
+
 }  // namespace fa

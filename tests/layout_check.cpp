@@ -11,6 +11,8 @@
 //  * the P^T / dS^T tile layout is a bijection, its XOR steps hold, and the
 //    chunks a producer writes reach the consumer as an A operand in the same
 //    contraction order as the transpose-read B operand;
+//  * the epilogues' staging layout covers its 32 rows exactly once and
+//    hands every reader its piece's halves in order;
 //  * every one of those accesses is free of bank conflicts when the LDS
 //    serves 16-byte accesses 8 lanes (8-byte accesses 16 lanes) per cycle
 //    over 32 banks, and 16 (32) lanes over 64 banks.
@@ -183,10 +185,52 @@ static void check_pt() {
       }
 }
 
+// Epilogue staging of 32 rows of D bf16: the 8-byte halves the lanes write
+// and the 16-byte pieces read back cover each row exactly once, the read
+// hands the halves back in order once stage_swap undoes the swap, and both
+// access kinds are conflict free.
+template <int D>
+static void check_stage() {
+  constexpr int NCH = D / 8, ROWB = 2 * D, RPI = 64 / NCH;
+  std::vector<int> seen(32 * ROWB / 8, 0);
+  for (int r = 0; r < 32; ++r)
+    for (int p = 0; p < NCH; ++p)
+      for (int h = 0; h < 2; ++h) {
+        const int off = stage_off<D>(r, p, h);
+        CHECK(off % 8 == 0 && off >= r * ROWB && off < (r + 1) * ROWB, "D=%d stage_off(%d,%d,%d)=%d outside its row", D,
+              r, p, h, off);
+        if (off % 8 || off < 0 || off >= 32 * ROWB) continue;
+        ++seen[off / 8];
+      }
+  for (size_t w = 0; w < seen.size(); ++w) CHECK(seen[w] == 1, "D=%d staging word %zu used %d times", D, w, seen[w]);
+  // writes: lane l, row l % 32, half l / 32 of piece 4 db + g4
+  for (int db = 0; db < D / 32; ++db)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      std::vector<int> addr(64);
+      for (int l = 0; l < 64; ++l) addr[l] = stage_off<D>(l & 31, 4 * db + g4, l >> 5);
+      CHECK(conflict_free(addr, 8), "D=%d staging writes db=%d g4=%d conflict", D, db, g4);
+    }
+  // reads: lane l, piece l % NCH of row RPI i + l / NCH, as one aligned
+  // 16-byte access whose halves come back in order after the swap
+  for (int i = 0; i < 32 / RPI; ++i) {
+    std::vector<int> addr(64);
+    for (int l = 0; l < 64; ++l) {
+      const int r = RPI * i + l / NCH, pc = l % NCH;
+      addr[l] = stage_off<D>(r, pc, 0) & ~15;
+      const int first = stage_swap<D>(r) ? 1 : 0;  // the half at the lower address
+      CHECK(stage_off<D>(r, pc, first) == addr[l] && stage_off<D>(r, pc, 1 - first) == addr[l] + 8,
+            "D=%d staging read row %d piece %d", D, r, pc);
+    }
+    CHECK(conflict_free(addr, 16), "D=%d staging reads i=%d conflict", D, i);
+  }
+}
+
 int main() {
   check_row_groups<64>();
   check_row_groups<128>();
   check_pt();
+  check_stage<64>();
+  check_stage<128>();
   if (fails) {
     std::printf("%d layout checks failed\n", fails);
     return 1;
