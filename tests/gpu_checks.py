@@ -62,3 +62,21 @@ def check_gradients(inp, causal, scale, window, o, lse, grads):
     assert np.all(got[0][:, e] == 0.0), "rows without a visible key must give dQ = 0"
     for name, g, r, dt, sl in zip(("dQ", "dK", "dV"), got, ref, det, slack):
         compare_model(name, g, r, dt, sl)
+
+
+def check_decode(fa, inp, causal, scale, window=0, num_splits=0):
+    """Split-KV decoding (fa_fwd_decode) against the oracle, with the
+    forward's rules."""
+    import torch
+
+    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
+    o, lse = fa.decode(q, k, v, causal=causal, scale=scale, window=window, num_splits=num_splits)
+    torch.cuda.synchronize()
+    o_np, lse_np = to_numpy_f32(o), lse.cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal, window=window)
+    e = empty_rows(inp, causal, window)
+    assert np.all(o_np[:, e] == 0.0), "rows without a visible key must give O = 0"
+    assert np.all(np.isneginf(lse_np[:, :, e])), "rows without a visible key must give LSE = -inf"
+    compare("O", o_np[:, ~e], o_ref[:, ~e], TOL_O, TOL_O_MEAN)
+    compare("LSE", lse_np[:, :, ~e], lse_ref[:, :, ~e], TOL_LSE, ulp_aware=False)
+    return o, lse

@@ -9,11 +9,9 @@ gates, rows without a visible key exactly O = 0 and LSE = -inf).
 
 import math
 
-import numpy as np
 import pytest
 
-import oracle
-from gpu_checks import empty_rows
+from gpu_checks import check_decode
 from io_aware_tiled_fa_amd.inputs import make_inputs
 from parity import TOL_LSE, TOL_O, TOL_O_MEAN, announce, compare, to_device, to_numpy_f32
 
@@ -30,22 +28,6 @@ def fa():
 
     binding.load_library()
     return binding
-
-
-def check_decode(fa, inp, causal, scale, window=0, num_splits=0):
-    import torch
-
-    q, k, v = (to_device(getattr(inp, n + "_bits")) for n in ("q", "k", "v"))
-    o, lse = fa.decode(q, k, v, causal=causal, scale=scale, window=window, num_splits=num_splits)
-    torch.cuda.synchronize()
-    o_np, lse_np = to_numpy_f32(o), lse.cpu().numpy().astype(np.float64)
-    o_ref, lse_ref = oracle.attention_forward(inp.q, inp.k, inp.v, scale, causal, window=window)
-    e = empty_rows(inp, causal, window)
-    assert np.all(o_np[:, e] == 0.0), "rows without a visible key must give O = 0"
-    assert np.all(np.isneginf(lse_np[:, :, e])), "rows without a visible key must give LSE = -inf"
-    compare("O", o_np[:, ~e], o_ref[:, ~e], TOL_O, TOL_O_MEAN)
-    compare("LSE", lse_np[:, :, ~e], lse_ref[:, :, ~e], TOL_LSE, ulp_aware=False)
-    return o, lse
 
 
 CASES = [
