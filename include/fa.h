@@ -52,8 +52,9 @@
  *    keys ending at its own position (itself and the W - 1 before it).
  *  - stream is a hipStream_t (NULL = the legacy default stream).  Calls only
  *    enqueue work and return; results are valid once the stream is
- *    synchronised.  The library allocates no memory and keeps no state
- *    beyond its loaded kernels.
+ *    synchronised.  The library allocates no memory; besides its loaded
+ *    kernels, its only state is the fixed scratch array of fa_bwd_noalloc
+ *    (one per GPU, below) and that array's address per device.
  *  - Every argument is validated before any HIP call.  On a bad argument
  *    nothing is launched and a negative FA_ERR_* code is returned.  A failed
  *    launch returns FA_ERR_LAUNCH.
